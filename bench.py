@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA position-independent KV path on one MI355X.
+
+One step is the per-batch GPU work of the path on the rotate-gather workload
+(64 requests x 32768 assembled tokens from a 4096-chunk registry, chunk
+lengths uniform in [32, 512], 80% registry hits): the per-entry trig pass and
+the rotate-gather kernel, with the chunk table's device image and the pool
+already resident in HBM.  ``value`` is assembled KV tokens per second.
+
+Further legs time MLA decode with rotation on load (batch 64 x 8192 tokens
+x 16 heads; batch 32 x 32768 x 128 heads with 16 splits) and the chunked
+tail-prefill (4096 queries over 65536 rows, 16 heads) with the same
+methodology, each with its own roofline.  The CPU oracle is timed on a
+bounded sample of the rotate-gather batch as ``cpu_baseline``.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "assembled KV tokens/s and MLA decode GB/s (% of HBM peak) vs CPU oracle"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+ROW_BYTES = 1152
+KERNEL_SOURCE = os.path.join(ROOT, "mla_position_independent_amd", "csrc", "irm_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_leg(fn, steps: int, warmup: int, inner_events: bool = True):
+    """Run fn(ev_mid_or_None) warmup+steps times.  Returns wall ms per step
+    (synchronised on both sides of the timed region) and the mean event time
+    of the part fn brackets (ms)."""
+    import torch
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        fn(evs[k] if inner_events else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = [a.elapsed_time(b) for a, b in evs] if inner_events else []
+    return (t1 - t0) * 1e3 / steps, (sum(kern) / len(kern)) if kern else None
+
+
+def leg_gather(args, irm, torch, synth):
+    log("rotate-gather: generating 64 x 32768-token batch")
+    w = synth.rotate_gather_batch()
+    pool = irm.to_device_bf16(w.pool)
+    inv = irm.rope_inv_freq(w.theta)
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(inv)
+    out = torch.empty((t.total_rows, 576), dtype=torch.bfloat16, device="cuda")
+
+    def step(ev):
+        t.set_rope(inv)                     # per-entry trig (double sincos)
+        if ev is not None:
+            ev[0].record()
+        irm.rotate_gather(t, pool, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    tokens = t.total_rows
+    alg_bytes = 2 * ROW_BYTES * tokens
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic("rotate_gather_kernel")
+    log(f"rotate-gather: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms, {achieved:.0f} GB/s")
+    res = {
+        "tokens": tokens, "ms_per_step": ms, "kernel_ms": kern_ms,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "rotate_gather_kernel",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "workload": w, "table": t,
+    }
+    return res
+
+
+def leg_decode(args, irm, torch, synth, name, make):
+    log(f"{name}: generating")
+    w = make()
+    pool = irm.to_device_bf16(w.pool)
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(irm.rope_inv_freq(w.theta))
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    H = w.n_heads
+    out = torch.empty((w.n_seq, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(irm.decode_workspace_bytes(t, H, w.n_splits), dtype=torch.uint8, device="cuda")
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        irm.mla_decode(ql, qr, t, pool, n_splits=w.n_splits, scale=w.scale, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    kv = ROW_BYTES * t.total_rows
+    qo = w.n_seq * H * (576 + 512) * 2
+    alg_bytes = kv + qo
+    flops = 2 * (576 + 512) * H * t.total_rows
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"{name}: {kern_ms:.3f} ms/call, {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s")
+    return {
+        "workload": w.name, "ms_per_call": round(kern_ms, 4), "tokens": t.total_rows, "n_splits": w.n_splits,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_split_kernel:" + w.name),
+                     "kernel": "decode_split_kernel + decode_combine_kernel",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+    }
+
+
+def leg_prefill(args, irm, torch, synth):
+    log("tail-prefill: generating")
+    w = synth.tail_prefill()
+    pool = irm.to_device_bf16(w.pool)
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(irm.rope_inv_freq(w.theta))
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    nq, H = w.q_lat.shape[0], w.n_heads
+    out = torch.empty((nq, H, 512), dtype=torch.bfloat16, device="cuda")
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        irm.mla_prefill_tail(ql, qr, w.q_pos0, t, pool, scale=w.scale, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kern_ms = time_leg(step, max(2, args.steps // 4), min(args.warmup, 2))
+    pairs = nq * w.q_pos0 + nq * (nq + 1) // 2      # visible (query, key) pairs
+    flops = pairs * H * 2 * (576 + 512)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    log(f"tail-prefill: {kern_ms:.3f} ms/call, {achieved:.0f} TFLOP/s")
+    return {
+        "workload": w.name, "ms_per_call": round(kern_ms, 4), "queries": nq, "kv_rows": t.total_rows,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                     "traffic": measured_traffic("prefill_kernel"), "kernel": "prefill_kernel",
+                     "algorithmic_flops_per_launch": flops},
+    }
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle, single-threaded, on the first requests of the rotate-gather
+    batch until ``seconds`` of CPU work have been spent (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    inv = oracle.rope_inv_freq(w.theta)
+    done_tokens, done_req, spent = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while done_req < w.n_seq and (spent < seconds or done_req == 0):
+            s = done_req
+            lo, hi = int(w.seq_first[s]), int(w.seq_first[s + 1])
+            sub = w.chunks[lo:hi]
+            t0 = time.perf_counter()
+            (g, d, _), = oracle.expand_table(sub, np.array([0, hi - lo]), w.pool.shape[0])
+            c, k = oracle.assemble_rows(w.pool, g, d, inv)
+            spent += time.perf_counter() - t0
+            done_tokens += g.shape[0]
+            done_req += 1
+    return {"value": round(done_tokens / spent, 1), "unit": "assembled KV tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {done_req} of {w.n_seq} requests ({done_tokens} tokens), "
+                      f"{spent:.1f} s single-threaded float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="gather,decode,long_decode,prefill")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy (for scaling HBM counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by request "
+              "or sequence with no exchange, and this build measures the one-GPU share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_position_independent_amd as irm
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    irm.lib()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 1 GiB x 5")
+        return
+
+    legs = [x.strip() for x in args.legs.split(",") if x.strip()]
+    g = leg_gather(args, irm, torch, synth)
+    extra = {}
+    if "decode" in legs:
+        extra["decode"] = leg_decode(args, irm, torch, synth, "batched decode", synth.batched_decode)
+    if "long_decode" in legs:
+        extra["long_decode"] = leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)
+    if "prefill" in legs:
+        extra["prefill"] = leg_prefill(args, irm, torch, synth)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a sample of the rotate-gather batch")
+        cpu = cpu_baseline(g["workload"], args.cpu_seconds)
+
+    w = g["workload"]
+    line = {
+        "metric": METRIC,
+        "value": round(g["tokens"] / (g["ms_per_step"] * 1e-3), 1),
+        "unit": "assembled KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 rows; chunk tables from the pages' CDC bounds)",
+        "config": {"workload": w.name, "requests": w.n_seq, "tokens_per_request": 32768,
+                   "registry_chunks": w.meta["n_registry"], "chunk_len": "uniform[32,512]",
+                   "hit_fraction_by_entry": 0.8, "p_src_range": [0, 131072], "row": "576 x bf16",
+                   "step": "per-entry trig pass + rotate-gather, table and pool resident in HBM"},
+        "roofline": g["roofline"],
+        "cpu_baseline": cpu,
+        "legs": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

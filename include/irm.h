@@ -1,0 +1,229 @@
+/*
+ * irm.h - C ABI of the MLA position-independent KV path on MI355X (gfx950).
+ *
+ * The operations follow the Irminsul pages (arXiv:2605.05696):
+ *   - an MLA KV row is a 512-wide position-free latent c_KV plus a 64-wide
+ *     RoPE key slice k_r (gist.science summary, section 2.1; gentlecold.top
+ *     article, section 4);
+ *   - a registry hit stores (c_KV, k_r_base, p_src); placed at p_tgt it is
+ *     reused with k_r = R(delta) k_r_base, delta = p_tgt - p_src, because
+ *     R(delta) R(p_src) = R(p_tgt) (gist.science section 2.2; gentlecold.top
+ *     sections 4 and 15);
+ *   - segments are appended to the assembled cache in target order and
+ *     positions below 32 are always freshly prefilled (gentlecold.top
+ *     section 5 serve-path pseudocode and section 7; gist.science 2.2);
+ *   - attention is the absorbed-matmul MLA form: score = q_lat . c_KV +
+ *     q_rope . k_r, value = c_KV (gentlecold.top section 4).
+ *
+ * Conventions for every function:
+ *   - Every call returns an irm_status; no exception crosses the ABI.  On a
+ *     non-OK status irm_last_error() returns a message for the calling thread.
+ *   - Validation errors are returned synchronously before any GPU work.
+ *     Launch failures return IRM_EHIP; faults inside a kernel surface at the
+ *     caller's next synchronisation of the stream.
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory.  The library never allocates device
+ *     memory and never synchronises a stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - bf16 tensors are IEEE bfloat16 bit patterns; all float->bf16 rounding
+ *     on the GPU is round-to-nearest-even.
+ *   - The KV pool is bf16 [pool_rows][576], row = [c_KV 512 | k_r 64]
+ *     (1152 bytes, 16-byte aligned).
+ */
+#ifndef IRM_H
+#define IRM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IRM_OK = 0,
+  IRM_EINVAL = 1,       /* malformed argument or table entry */
+  IRM_ERANGE = 2,       /* pool row, position or delta out of range */
+  IRM_ELAYOUT = 3,      /* target positions not contiguous from 0 */
+  IRM_ECARVEOUT = 4,    /* a registry (non-fresh) row below position 32 */
+  IRM_EWORKSPACE = 5,   /* workspace missing or too small */
+  IRM_EUNSUPPORTED = 6, /* shape the kernels do not support */
+  IRM_EHIP = 7          /* HIP runtime error (launch, copy, device) */
+} irm_status;
+
+enum {
+  IRM_D_LATENT = 512,   /* c_KV width */
+  IRM_D_ROPE = 64,      /* k_r width: 32 interleaved pairs (2i, 2i+1) */
+  IRM_ROW = 576,        /* pool / assembled row width in bf16 elements */
+  IRM_CARVE_OUT = 32,   /* positions [0, 32) are never served from the registry */
+  IRM_MAX_HEADS = 128
+};
+
+#define IRM_FRESH 1u    /* irm_chunk.flags: rows freshly prefilled at p_tgt */
+
+/*
+ * One chunk-table entry, built on the host.  Entries of a sequence are listed
+ * in target order.  Row j (0 <= j < len) of the entry is assembled at
+ * position p_tgt + j from pool row pool_row + j; its k_r is rotated by
+ * delta = p_tgt - p_src (gentlecold.top section 5: one delta per segment).
+ * A fresh entry (flags & IRM_FRESH) holds rows prefilled at p_tgt, is copied
+ * verbatim and must have p_src == p_tgt.  An exact-prefix entry is a
+ * non-fresh entry with p_src == p_tgt (delta 0, copied verbatim).
+ * 20 bytes, no padding.
+ */
+typedef struct irm_chunk {
+  uint32_t pool_row;
+  uint32_t len;
+  int32_t p_src;
+  int32_t p_tgt;
+  uint32_t flags;
+} irm_chunk;
+
+typedef struct irm_table irm_table; /* opaque; owned by the library */
+
+/* Thread-local message for the last non-OK status of this thread ("" if none). */
+const char* irm_last_error(void);
+
+/*
+ * Standard RoPE inverse frequencies for the 64-wide k_r slice:
+ * inv_freq[i] = theta^(-2i/64), i = 0..31, in double precision.
+ * The pages stress that the rotation must use the model's own rotary
+ * frequencies (gentlecold.top section 11), so every entry point that rotates
+ * takes the 32 frequencies themselves; this helper covers plain RoPE.
+ * host out: inv_freq[32].  EINVAL if theta <= 1 or inv_freq is NULL.
+ */
+irm_status irm_rope_inv_freq(double theta, double* inv_freq);
+
+/*
+ * Validate a chunk table and build its device image in library-owned host
+ * memory.  Makes no HIP call (usable without a GPU).
+ *   host chunks[n_chunks]; host seq_first[n_seq + 1]: sequence s owns
+ *   entries [seq_first[s], seq_first[s+1]); seq_first[0] == 0 and
+ *   seq_first[n_seq] == n_chunks, nondecreasing.  An empty sequence is legal.
+ *   pool_rows: rows in the pool this table will be used with (the kernels
+ *   address at most 2^32 pool rows; larger values are treated as 2^32).
+ * Checks, per entry in order, returning the first failure:
+ *   unknown flag bits (EINVAL); len == 0 (EINVAL);
+ *   pool_row + len > pool_rows (ERANGE);
+ *   p_tgt != previous p_tgt + previous len, or != 0 for a sequence's first
+ *   entry (ELAYOUT); p_tgt + len - 1 > INT32_MAX (ERANGE);
+ *   fresh with p_src != p_tgt (EINVAL); non-fresh with p_tgt < 32 (ECARVEOUT);
+ *   delta outside int32 (ERANGE).  Total rows over all sequences must stay
+ *   below 2^31 (ERANGE).
+ * Output row of (sequence s, position p) in every assembled buffer is
+ * seq_base[s] + p, with seq_base the prefix sum of sequence lengths.
+ * *out receives the handle; free it with irm_table_destroy.
+ */
+irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunks,
+                            const uint32_t* seq_first, uint32_t n_seq,
+                            uint64_t pool_rows, irm_table** out);
+
+/* Frees the handle.  The device buffer given to irm_table_upload stays the
+ * caller's; destroy only after the stream is done with kernels using it. */
+irm_status irm_table_destroy(irm_table* t);
+
+/*
+ * Sizes of a table (any pointer may be NULL):
+ *   n_seq, n_chunks; total_rows = sum of lengths; max_seq_len;
+ *   device_bytes = size of the device image irm_table_upload needs.
+ */
+irm_status irm_table_info(const irm_table* t, uint32_t* n_seq, uint32_t* n_chunks,
+                          uint64_t* total_rows, uint32_t* max_seq_len,
+                          size_t* device_bytes);
+
+/* host out seq_base[n_seq + 1]: first assembled row of each sequence. */
+irm_status irm_table_seq_base(const irm_table* t, uint64_t* seq_base);
+
+/*
+ * Host-side expansion of the table, one value per assembled row (each array
+ * host, [total_rows], any may be NULL): the pool row it is gathered from,
+ * its delta (0 for fresh rows) and its fresh flag.  No HIP call.
+ */
+irm_status irm_table_expand_host(const irm_table* t, int64_t* pool_row, int32_t* delta,
+                                 uint8_t* fresh);
+
+/*
+ * Copy the device image to dev_buf (device, dev_bytes >= device_bytes,
+ * 256-byte aligned) on `stream` and compute, on the GPU in double precision,
+ * cos and sin of delta * inv_freq[i] for every entry and pair (stored as
+ * float).  host inv_freq[32].  The handle remembers dev_buf; every later call
+ * taking this table reads it there, ordered after this call on the same
+ * stream.  The host image stays valid until destroy, so the copy needs no
+ * synchronisation by the caller.  EWORKSPACE if dev_bytes is too small.
+ */
+irm_status irm_table_upload(irm_table* t, const double* inv_freq, void* dev_buf,
+                            size_t dev_bytes, void* stream);
+
+/*
+ * Recompute, on `stream`, the per-entry cos/sin of delta * inv_freq[i] of an
+ * uploaded table (the trig pass irm_table_upload also runs), e.g. for another
+ * model's rotary frequencies.  host inv_freq[32].  No host-to-device copy.
+ */
+irm_status irm_table_set_rope(irm_table* t, const double* inv_freq, void* stream);
+
+/*
+ * Device export of the gather map (device int64 pool_row[total_rows] and
+ * int32 delta[total_rows], either may be NULL).  Requires an uploaded table.
+ */
+irm_status irm_table_gather_index(const irm_table* t, int64_t* pool_row, int32_t* delta,
+                                  void* stream);
+
+/*
+ * Rotate-gather: assemble every sequence of the table into out_kv.
+ *   device pool bf16 [pool_rows][576] (pool_rows >= the table's pool_rows);
+ *   device out_kv bf16 [total_rows][576]: c_KV copied bit for bit; k_r
+ *   copied bit for bit for fresh and delta == 0 rows, else R(delta) k_r_base
+ *   computed in float and rounded to bf16;
+ *   device kr_f32 optional float [total_rows][64]: the rotated k_r before
+ *   rounding (NULL in production).
+ * Buffers must not overlap.  Requires an uploaded table.
+ */
+irm_status irm_rotate_gather(const irm_table* t, const void* pool, uint64_t pool_rows,
+                             void* out_kv, float* kr_f32, void* stream);
+
+/*
+ * Split-KV decode workspace size for a table, head count and split count
+ * (n_splits == 0 picks the library default; the same rule is used by
+ * irm_mla_decode).  *bytes receives the size (256-byte aligned pointer).
+ */
+irm_status irm_mla_decode_workspace(const irm_table* t, uint32_t n_heads, uint32_t n_splits,
+                                    size_t* bytes);
+
+/*
+ * Absorbed MLA decode, one query token per sequence, over the cache the table
+ * assembles, with k_r rotated on load (no assembled buffer is written).
+ *   device q_latent bf16 [n_seq][n_heads][512]; device q_rope bf16
+ *   [n_seq][n_heads][64] (already RoPE'd at the query position);
+ *   device out bf16 [n_seq][n_heads][512]; device lse optional float
+ *   [n_seq][n_heads] (natural-log sum of exp of the scaled scores);
+ *   n_heads a multiple of 16, <= 128 (else EUNSUPPORTED); scale > 0 finite;
+ *   n_splits: KV splits per sequence (0 = default); every sequence must hold
+ *   at least one row (EINVAL).
+ *   device workspace of at least irm_mla_decode_workspace bytes (EWORKSPACE).
+ * Each query attends to every row of its sequence.
+ */
+irm_status irm_mla_decode(const void* q_latent, const void* q_rope, const irm_table* t,
+                          const void* pool, uint64_t pool_rows, uint32_t n_heads,
+                          uint32_t n_splits, float scale, void* out, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Chunked tail-prefill for one sequence (the table must hold exactly one
+ * sequence of N rows): n_q query tokens at positions q_pos0 .. q_pos0+n_q-1
+ * attend causally (row t visible to query i iff t <= q_pos0 + i) over the
+ * assembled cache, with k_r rotated on load.
+ *   device q_latent bf16 [n_q][n_heads][512]; q_rope bf16 [n_q][n_heads][64];
+ *   device out bf16 [n_q][n_heads][512]; lse optional float [n_q][n_heads].
+ *   0 <= q_pos0, 1 <= n_q, q_pos0 + n_q <= N (ERANGE); n_heads a multiple of
+ *   16, <= 128 (EUNSUPPORTED).
+ */
+irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_rope, int32_t q_pos0,
+                                uint32_t n_q, const irm_table* t, const void* pool,
+                                uint64_t pool_rows, uint32_t n_heads, float scale,
+                                void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IRM_H */

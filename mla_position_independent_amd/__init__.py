@@ -1,0 +1,277 @@
+"""Python binding of libirm (MLA position-independent KV path on MI355X).
+
+Thin ctypes marshalling over the C ABI in include/irm.h: every step of the
+path runs in the HIP kernels of libirm.so.  torch is used only for device
+memory and streams.  Importing this package does not load the library;
+the first call does, and raises if libirm.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libirm.so")
+
+D_LATENT = 512
+D_ROPE = 64
+ROW = 576
+CARVE_OUT = 32
+FRESH = 1
+DEFAULT_SCALE = 1.0 / math.sqrt(192.0)
+
+STATUS = {0: "OK", 1: "EINVAL", 2: "ERANGE", 3: "ELAYOUT", 4: "ECARVEOUT",
+          5: "EWORKSPACE", 6: "EUNSUPPORTED", 7: "EHIP"}
+
+CHUNK_DTYPE = np.dtype(
+    [("pool_row", "<u4"), ("len", "<u4"), ("p_src", "<i4"), ("p_tgt", "<i4"), ("flags", "<u4")]
+)
+
+EXPORTS = (
+    "irm_last_error", "irm_rope_inv_freq", "irm_table_create", "irm_table_destroy",
+    "irm_table_info", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
+    "irm_table_set_rope",
+    "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
+    "irm_mla_decode", "irm_mla_prefill_tail",
+)
+
+
+class IrmError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        self.status = status
+        self.code = STATUS.get(status, str(status))
+        super().__init__(f"{fn}: {self.code}: {msg}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libirm.so (built in-tree by _build.build()); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python mla_position_independent_amd/_build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, u32, u64, i32, sz = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "irm_last_error": (ctypes.c_char_p, []),
+        "irm_rope_inv_freq": (ctypes.c_int, [ctypes.c_double, vp]),
+        "irm_table_create": (ctypes.c_int, [vp, u32, vp, u32, u64, P(vp)]),
+        "irm_table_destroy": (ctypes.c_int, [vp]),
+        "irm_table_info": (ctypes.c_int, [vp, P(u32), P(u32), P(u64), P(u32), P(sz)]),
+        "irm_table_seq_base": (ctypes.c_int, [vp, vp]),
+        "irm_table_expand_host": (ctypes.c_int, [vp, vp, vp, vp]),
+        "irm_table_upload": (ctypes.c_int, [vp, vp, vp, sz, vp]),
+        "irm_table_set_rope": (ctypes.c_int, [vp, vp, vp]),
+        "irm_table_gather_index": (ctypes.c_int, [vp, vp, vp, vp]),
+        "irm_rotate_gather": (ctypes.c_int, [vp, vp, u64, vp, vp, vp]),
+        "irm_mla_decode_workspace": (ctypes.c_int, [vp, u32, u32, P(sz)]),
+        "irm_mla_decode": (ctypes.c_int, [vp, vp, vp, vp, u64, u32, u32, ctypes.c_float, vp, vp, vp, sz, vp]),
+        "irm_mla_prefill_tail": (ctypes.c_int, [vp, vp, i32, u32, vp, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(st: int, fn: str):
+    if st != 0:
+        raise IrmError(st, fn, lib().irm_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def rope_inv_freq(theta: float = 10000.0) -> np.ndarray:
+    """theta^(-2i/64), i = 0..31, computed by the library."""
+    out = np.zeros(32, dtype=np.float64)
+    _check(lib().irm_rope_inv_freq(float(theta), out.ctypes.data), "irm_rope_inv_freq")
+    return out
+
+
+class Table:
+    """A validated chunk table (host image) and, after upload(), its device copy."""
+
+    def __init__(self, chunks: np.ndarray, seq_first: np.ndarray, pool_rows: int):
+        chunks = np.ascontiguousarray(chunks, dtype=CHUNK_DTYPE)
+        seq_first = np.ascontiguousarray(seq_first, dtype=np.uint32)
+        self._h = ctypes.c_void_p()
+        L = lib()
+        _check(L.irm_table_create(chunks.ctypes.data if chunks.size else None, chunks.shape[0],
+                                  seq_first.ctypes.data, seq_first.shape[0] - 1, int(pool_rows),
+                                  ctypes.byref(self._h)), "irm_table_create")
+        n_seq, n_chunks, mx = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+        total, dbytes = ctypes.c_uint64(), ctypes.c_size_t()
+        _check(L.irm_table_info(self._h, ctypes.byref(n_seq), ctypes.byref(n_chunks), ctypes.byref(total),
+                                ctypes.byref(mx), ctypes.byref(dbytes)), "irm_table_info")
+        self.n_seq, self.n_chunks = n_seq.value, n_chunks.value
+        self.total_rows, self.max_seq_len, self.device_bytes = total.value, mx.value, dbytes.value
+        self.pool_rows = int(pool_rows)
+        self._dev = None
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().irm_table_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def seq_base(self) -> np.ndarray:
+        out = np.zeros(self.n_seq + 1, dtype=np.uint64)
+        _check(lib().irm_table_seq_base(self._h, out.ctypes.data), "irm_table_seq_base")
+        return out
+
+    def expand_host(self) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        n = self.total_rows
+        pr = np.zeros(n, np.int64)
+        de = np.zeros(n, np.int32)
+        fr = np.zeros(n, np.uint8)
+        _check(lib().irm_table_expand_host(self._h, pr.ctypes.data, de.ctypes.data, fr.ctypes.data),
+               "irm_table_expand_host")
+        return pr, de, fr
+
+    def upload(self, inv_freq: Optional[np.ndarray] = None, dev_buf=None, stream=None) -> "Table":
+        """Copy the device image to dev_buf (a torch uint8 CUDA tensor; allocated
+        here if None) and compute the per-entry trig on the GPU."""
+        import torch
+        if inv_freq is None:
+            inv_freq = rope_inv_freq(10000.0)
+        inv = np.ascontiguousarray(inv_freq, dtype=np.float64)
+        assert inv.shape == (32,)
+        if dev_buf is None:
+            dev_buf = torch.empty(max(self.device_bytes, 256), dtype=torch.uint8, device="cuda")
+        _check(lib().irm_table_upload(self._h, inv.ctypes.data, _ptr(dev_buf), dev_buf.numel(),
+                                      _stream(stream)), "irm_table_upload")
+        self._dev = dev_buf
+        self._inv = inv
+        return self
+
+    def set_rope(self, inv_freq: np.ndarray, stream=None) -> "Table":
+        """Recompute the per-entry cos/sin on the GPU (no host-to-device copy)."""
+        inv = np.ascontiguousarray(inv_freq, dtype=np.float64)
+        assert inv.shape == (32,)
+        _check(lib().irm_table_set_rope(self._h, inv.ctypes.data, _stream(stream)), "irm_table_set_rope")
+        self._inv = inv
+        return self
+
+    def gather_index(self, stream=None):
+        import torch
+        pr = torch.empty(self.total_rows, dtype=torch.int64, device="cuda")
+        de = torch.empty(self.total_rows, dtype=torch.int32, device="cuda")
+        _check(lib().irm_table_gather_index(self._h, _ptr(pr), _ptr(de), _stream(stream)),
+               "irm_table_gather_index")
+        return pr, de
+
+
+def _bf16_2d(t, cols: int, name: str):
+    import torch
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 bits (bfloat16/int16/uint16), got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous() or t.shape[-1] != cols:
+        raise ValueError(f"{name} must be a contiguous CUDA tensor with last dim {cols}")
+
+
+def rotate_gather(table: Table, pool, out=None, kr_f32: bool = False, stream=None):
+    """Assemble every sequence of ``table`` from ``pool`` (bf16 [rows][576]).
+    Returns out (bf16 [total_rows][576]) and, if kr_f32, the float rotated k_r."""
+    import torch
+    _bf16_2d(pool, ROW, "pool")
+    if out is None:
+        out = torch.empty((table.total_rows, ROW), dtype=torch.bfloat16, device=pool.device)
+    kr = torch.empty((table.total_rows, D_ROPE), dtype=torch.float32, device=pool.device) if kr_f32 else None
+    _check(lib().irm_rotate_gather(table.handle, _ptr(pool), pool.shape[0], _ptr(out), _ptr(kr),
+                                   _stream(stream)), "irm_rotate_gather")
+    return (out, kr) if kr_f32 else out
+
+
+def decode_workspace_bytes(table: Table, n_heads: int, n_splits: int = 0) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().irm_mla_decode_workspace(table.handle, n_heads, n_splits, ctypes.byref(b)),
+           "irm_mla_decode_workspace")
+    return b.value
+
+
+def mla_decode(q_lat, q_rope, table: Table, pool, n_splits: int = 0, scale: float = DEFAULT_SCALE,
+               out=None, want_lse: bool = False, workspace=None, stream=None):
+    """Absorbed MLA decode with k_r rotated on load.  q_lat bf16 [B][H][512],
+    q_rope bf16 [B][H][64].  Returns out bf16 [B][H][512] (and lse [B][H])."""
+    import torch
+    _bf16_2d(pool, ROW, "pool")
+    _bf16_2d(q_lat, D_LATENT, "q_lat")
+    _bf16_2d(q_rope, D_ROPE, "q_rope")
+    B, H = q_lat.shape[0], q_lat.shape[1]
+    if B != table.n_seq or tuple(q_rope.shape) != (B, H, D_ROPE):
+        raise ValueError("q_lat/q_rope must be [n_seq][H][512] / [n_seq][H][64]")
+    if out is None:
+        out = torch.empty((B, H, D_LATENT), dtype=torch.bfloat16, device=pool.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=pool.device) if want_lse else None
+    need = decode_workspace_bytes(table, H, n_splits)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=pool.device)
+    _check(lib().irm_mla_decode(_ptr(q_lat), _ptr(q_rope), table.handle, _ptr(pool), pool.shape[0], H,
+                                n_splits, float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "irm_mla_decode")
+    return (out, lse) if want_lse else out
+
+
+def mla_prefill_tail(q_lat, q_rope, q_pos0: int, table: Table, pool, scale: float = DEFAULT_SCALE,
+                     out=None, want_lse: bool = False, stream=None):
+    """Causal tail-prefill of n_q queries at q_pos0.. over the one sequence of
+    ``table``.  q_lat bf16 [n_q][H][512], q_rope [n_q][H][64]."""
+    import torch
+    _bf16_2d(pool, ROW, "pool")
+    _bf16_2d(q_lat, D_LATENT, "q_lat")
+    _bf16_2d(q_rope, D_ROPE, "q_rope")
+    nq, H = q_lat.shape[0], q_lat.shape[1]
+    if tuple(q_rope.shape) != (nq, H, D_ROPE):
+        raise ValueError("q_rope must be [n_q][H][64]")
+    if out is None:
+        out = torch.empty((nq, H, D_LATENT), dtype=torch.bfloat16, device=pool.device)
+    lse = torch.empty((nq, H), dtype=torch.float32, device=pool.device) if want_lse else None
+    _check(lib().irm_mla_prefill_tail(_ptr(q_lat), _ptr(q_rope), int(q_pos0), nq, table.handle, _ptr(pool),
+                                      pool.shape[0], H, float(scale), _ptr(out), _ptr(lse),
+                                      _stream(stream)), "irm_mla_prefill_tail")
+    return (out, lse) if want_lse else out
+
+
+def to_device_bf16(bits: np.ndarray):
+    """uint16 bf16 bit patterns (host) -> torch.bfloat16 CUDA tensor."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def from_device_bf16(t) -> np.ndarray:
+    """torch bf16 CUDA tensor -> uint16 bit patterns (host)."""
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

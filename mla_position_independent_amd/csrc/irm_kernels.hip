@@ -1,0 +1,827 @@
+// HIP kernels (gfx950) and the C ABI entry points that launch them.
+//
+// Operations follow the Irminsul pages (arXiv:2605.05696):
+//  * delta rotation k_r = R(p_tgt - p_src) k_r_base of the 64-wide RoPE slice,
+//    with c_KV reused unchanged (gist.science summary 2.1-2.2; gentlecold.top
+//    article sections 4, 5 and 15);
+//  * absorbed MLA attention: score = q_lat . c_KV + q_rope . k_r, value = c_KV
+//    (gentlecold.top section 4), rotating k_r while the KV tile is loaded, the
+//    fusion the pages propose for the HBM-to-on-chip load (gist.science 2.2
+//    and 4; gentlecold.top sections 5 and 14.1).
+//
+// Data layout: pool and assembled rows are bf16 [rows][576] = 72 units of
+// 16 bytes; units 0..63 are c_KV, units 64..71 are k_r (4 rotation pairs per
+// unit).  Angles are formed and their sine/cosine evaluated in double once per
+// table entry (delta reaches 2^17, where a float angle is off by ~1e-2 rad);
+// only the 2x2 rotation itself runs in float.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "irm_internal.h"
+
+using irm::DevEntry;
+using irm::fail;
+
+namespace {
+
+constexpr int kRowBytes = IRM_ROW * 2;                       // 1152
+constexpr int kUnitsPerRow = kRowBytes / 16;                 // 72
+constexpr int kLatUnits = IRM_D_LATENT * 2 / 16;             // 64
+constexpr int kThreads = 256;                                // 4 waves of 64
+constexpr int kTile = 64;                                    // KV rows per tile
+constexpr int kUnitsPerThread = kTile * kUnitsPerRow / kThreads;  // 18
+constexpr int kLdsRow = kRowBytes + 32;                      // padded LDS row stride
+constexpr uint32_t kNoRot = 0xffffffffu;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+struct InvFreq {
+  double w[irm::kPairs];
+};
+
+struct Image {
+  const DevEntry* ents;
+  const uint32_t* seq_first;
+  const uint32_t* seq_base;
+  const uint32_t* block_map;
+  const float2* trig;
+};
+
+Image image_of(const irm_table* t) {
+  const unsigned char* d = static_cast<const unsigned char*>(t->dev);
+  Image im;
+  im.ents = reinterpret_cast<const DevEntry*>(d + t->layout.off_entries);
+  im.seq_first = reinterpret_cast<const uint32_t*>(d + t->layout.off_seq_first);
+  im.seq_base = reinterpret_cast<const uint32_t*>(d + t->layout.off_seq_base);
+  im.block_map = reinterpret_cast<const uint32_t*>(d + t->layout.off_block_map);
+  im.trig = reinterpret_cast<const float2*>(d + t->layout.off_trig);
+  return im;
+}
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Entry that holds assembled row g: start at the block map, walk forward.
+__device__ __forceinline__ uint32_t find_entry(const Image& im, uint32_t g) {
+  uint32_t e = im.block_map[g / irm::kBlockRows];
+  while (g >= im.ents[e].out_row + im.ents[e].len) ++e;
+  return e;
+}
+
+// Rotate the 4 pairs of one k_r unit; pair p uses (cos, sin) = tr[p].
+// x' = x cos - y sin, y' = x sin + y cos, in float.
+__device__ __forceinline__ void rotate_unit_f32(const uint4& w, const float2* tr, float (&f)[8]) {
+  const uint32_t word[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float x = bf16_lo(word[p]), y = bf16_hi(word[p]);
+    const float2 cs = tr[p];
+    f[2 * p] = fmaf(x, cs.x, -(y * cs.y));
+    f[2 * p + 1] = fmaf(x, cs.y, y * cs.x);
+  }
+}
+
+__device__ __forceinline__ uint4 rotate_unit(const uint4& w, const float2* tr) {
+  float f[8];
+  rotate_unit_f32(w, tr, f);
+  return make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+                    pack_bf16(f[6], f[7]));
+}
+
+// ---------------------------------------------------------------------------
+// trig prepass: cos/sin(delta_e * w_i) in double, stored as float2
+// ---------------------------------------------------------------------------
+__global__ void trig_kernel(const DevEntry* __restrict__ ents, uint32_t n_entries, InvFreq f,
+                            float2* __restrict__ trig) {
+  const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_entries * irm::kPairs) return;
+  const uint32_t e = idx / irm::kPairs, i = idx % irm::kPairs;
+  const double phi = (double)ents[e].delta * f.w[i];
+  double s, c;
+  sincos(phi, &s, &c);
+  trig[idx] = make_float2((float)c, (float)s);
+}
+
+// ---------------------------------------------------------------------------
+// gather index export
+// ---------------------------------------------------------------------------
+__global__ void gather_index_kernel(Image im, uint32_t total_rows, int64_t* __restrict__ pool_row,
+                                    int32_t* __restrict__ delta) {
+  const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= total_rows) return;
+  const uint32_t e = find_entry(im, g);
+  const DevEntry d = im.ents[e];
+  if (pool_row) pool_row[g] = (int64_t)d.pool_row + (g - d.out_row);
+  if (delta) delta[g] = d.delta;
+}
+
+// ---------------------------------------------------------------------------
+// rotate-gather: one workgroup per 64 assembled rows, flat 16-byte units
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void rotate_gather_kernel(Image im, uint32_t total_rows,
+                                                                  const uint4* __restrict__ pool,
+                                                                  uint4* __restrict__ out,
+                                                                  float* __restrict__ kr_f32) {
+  __shared__ uint32_t s_src[kTile];
+  __shared__ uint32_t s_rot[kTile];
+  const uint32_t tile0 = blockIdx.x * kTile;
+  const int tid = threadIdx.x;
+  const uint32_t nrows = min((uint32_t)kTile, total_rows - tile0);
+  if (tid < kTile) {
+    uint32_t src = 0, rot = kNoRot;
+    if ((uint32_t)tid < nrows) {
+      const uint32_t g = tile0 + tid;
+      const uint32_t e = find_entry(im, g);
+      const DevEntry d = im.ents[e];
+      src = d.pool_row + (g - d.out_row);
+      rot = d.delta != 0 ? e : kNoRot;
+    }
+    s_src[tid] = src;
+    s_rot[tid] = rot;
+  }
+  __syncthreads();
+  const uint32_t nunits = nrows * kUnitsPerRow;
+  uint4 v[kUnitsPerThread];
+#pragma unroll
+  for (int k = 0; k < kUnitsPerThread; ++k) {
+    const uint32_t u = tid + k * kThreads;
+    if (u < nunits) {
+      const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
+      v[k] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                                            pool + (size_t)s_src[r] * kUnitsPerRow + c)));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kUnitsPerThread; ++k) {
+    const uint32_t u = tid + k * kThreads;
+    if (u < nunits) {
+      const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
+      uint4 w = v[k];
+      if (c >= (uint32_t)kLatUnits) {
+        const uint32_t e = s_rot[r];
+        float f[8];
+        if (e != kNoRot) {
+          rotate_unit_f32(w, im.trig + (size_t)e * irm::kPairs + (c - kLatUnits) * 4, f);
+          w = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+                         pack_bf16(f[6], f[7]));
+        } else {
+          f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+          f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+        }
+        if (kr_f32) {
+          float4* dst = reinterpret_cast<float4*>(kr_f32 + (size_t)(tile0 + r) * IRM_D_ROPE +
+                                                  (c - kLatUnits) * 8);
+          dst[0] = make_float4(f[0], f[1], f[2], f[3]);
+          dst[1] = make_float4(f[4], f[5], f[6], f[7]);
+        }
+      }
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, w),
+                                  reinterpret_cast<u32x4_t*>(out + (size_t)(tile0 + r) * kUnitsPerRow + c));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention building blocks (shared by decode and tail-prefill)
+//
+// A workgroup of 4 waves streams KV tiles of 64 rows through LDS (padded
+// row-major, c_KV and rotated k_r).  The score block of 16 rows x 16 heads
+// is S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T from
+// registers), so each lane ends with 4 rows of one head; P^T in that layout
+// is directly the B operand of v_mfma_f32_16x16x16_bf16 for O^T = C^T P^T,
+// whose C^T operand is read column-wise from LDS.  O^T leaves every lane with
+// 128 outputs of a single head, so the online-softmax rescale is lane-local.
+// Softmax runs in the base-2 domain (scores pre-multiplied by scale*log2 e).
+// ---------------------------------------------------------------------------
+
+// Row info of a tile: pool row and rotation entry (or kNoRot) per tile row.
+__device__ __forceinline__ void tile_row_info(const Image& im, uint32_t g0, uint32_t nrows,
+                                              uint32_t* s_src, uint32_t* s_rot) {
+  const int t = threadIdx.x;
+  if (t < kTile) {
+    uint32_t src = 0, rot = kNoRot;
+    if ((uint32_t)t < nrows) {
+      const uint32_t g = g0 + t;
+      const uint32_t e = find_entry(im, g);
+      const DevEntry d = im.ents[e];
+      src = d.pool_row + (g - d.out_row);
+      rot = d.delta != 0 ? e : kNoRot;
+    }
+    s_src[t] = src;
+    s_rot[t] = rot;
+  }
+}
+
+// Issue the global loads of one tile into registers (rows >= nrows read as 0).
+__device__ __forceinline__ void load_tile(const uint4* __restrict__ pool, const uint32_t* s_src,
+                                          uint32_t nrows, uint4 (&v)[kUnitsPerThread]) {
+  const uint32_t nunits = nrows * kUnitsPerRow;
+#pragma unroll
+  for (int k = 0; k < kUnitsPerThread; ++k) {
+    const uint32_t u = threadIdx.x + k * kThreads;
+    if (u < nunits) {
+      const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
+      v[k] = pool[(size_t)s_src[r] * kUnitsPerRow + c];
+    } else {
+      v[k] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Rotate the k_r units held in registers (reads s_rot of the same tile).
+__device__ __forceinline__ void rotate_tile_regs(const float2* __restrict__ trig,
+                                                 const uint32_t* s_rot,
+                                                 uint4 (&v)[kUnitsPerThread]) {
+#pragma unroll
+  for (int k = 0; k < kUnitsPerThread; ++k) {
+    const uint32_t u = threadIdx.x + k * kThreads;
+    const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
+    if (c >= (uint32_t)kLatUnits) {
+      const uint32_t e = s_rot[r];
+      if (e != kNoRot) v[k] = rotate_unit(v[k], trig + (size_t)e * irm::kPairs + (c - kLatUnits) * 4);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile_lds(unsigned char* lds, const uint4 (&v)[kUnitsPerThread]) {
+#pragma unroll
+  for (int k = 0; k < kUnitsPerThread; ++k) {
+    const uint32_t u = threadIdx.x + k * kThreads;
+    const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
+    *reinterpret_cast<uint4*>(lds + r * kLdsRow + c * 16) = v[k];
+  }
+}
+
+// S^T for tile rows [row0, row0+16): lane (q = lane/16, r = lane%16) gets the
+// scores of rows row0 + 4q + i (i = 0..3) for head r.
+__device__ __forceinline__ f32x4_t qk_block(const unsigned char* lds, int row0,
+                                            const bf16x8_t (&qb)[18]) {
+  const int lane = threadIdx.x & 63;
+  const unsigned char* p = lds + (row0 + (lane & 15)) * kLdsRow + (lane >> 4) * 16;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 18; ++kk) {
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + kk * 64));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kk], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// O^T[n][head] += C^T[n][rows row0+4q..+3] P^T[rows][head] for all 512 n.
+__device__ __forceinline__ void pv_block(const unsigned char* lds, int row0, i16x4_t pb,
+                                         f32x4_t (&o)[32]) {
+  const int lane = threadIdx.x & 63;
+  const unsigned short* base =
+      reinterpret_cast<const unsigned short*>(lds + (row0 + 4 * (lane >> 4)) * kLdsRow) + (lane & 15);
+  constexpr int kStride = kLdsRow / 2;
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) {
+    i16x4_t a;
+    a.x = (short)base[16 * nb];
+    a.y = (short)base[kStride + 16 * nb];
+    a.z = (short)base[2 * kStride + 16 * nb];
+    a.w = (short)base[3 * kStride + 16 * nb];
+    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[nb], 0, 0, 0);
+  }
+}
+
+// Online softmax for one head per lane over `nb` blocks of 4 scores each.
+// s[] holds base-2 scaled scores (-inf where masked).  Updates m and the
+// lane-local partial l, rescales o when the max moved, and returns P^T
+// (bf16) per block in pb[].
+template <int NB>
+__device__ __forceinline__ void softmax_update(float (&s)[NB][4], float& m, float& l,
+                                               f32x4_t (&o)[32], i16x4_t (&pb)[NB]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = exp2f(m - m_use);  // m == -inf gives 0
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2f(s[j][i] - m_use);
+      sum += p[i];
+    }
+    pb[j].x = (short)bf16_rne(p[0]);
+    pb[j].y = (short)bf16_rne(p[1]);
+    pb[j].z = (short)bf16_rne(p[2]);
+    pb[j].w = (short)bf16_rne(p[3]);
+  }
+  l = l * alpha + sum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int nb = 0; nb < 32; ++nb) o[nb] *= alpha;
+  }
+  m = m_new;
+}
+
+// Q^T operands of one head group for one query: lane (q, r) holds head
+// g*16 + r, dims 32 kk + 8 q .. +8 (kk 0..15 latent, 16..17 rope).
+__device__ __forceinline__ void load_q(const uint4* __restrict__ q_lat, const uint4* __restrict__ q_rope,
+                                       uint32_t qrow, uint32_t n_heads, uint32_t head,
+                                       bf16x8_t (&qb)[18]) {
+  const int q = (threadIdx.x & 63) >> 4;
+  const uint4* pl = q_lat + ((size_t)qrow * n_heads + head) * (IRM_D_LATENT / 8) + q;
+  const uint4* pr = q_rope + ((size_t)qrow * n_heads + head) * (IRM_D_ROPE / 8) + q;
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) qb[kk] = __builtin_bit_cast(bf16x8_t, pl[4 * kk]);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = __builtin_bit_cast(bf16x8_t, pr[4 * kk]);
+}
+
+// ---------------------------------------------------------------------------
+// split-KV decode, pass 1
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  Image im;
+  const uint4* pool;
+  const uint4* q_lat;
+  const uint4* q_rope;
+  float* ws_acc;  // [n_seq][n_splits][n_heads][512], unnormalised
+  float* ws_ml;   // [n_seq][n_splits][n_heads][2]: base-2 max, sum
+  uint32_t n_seq, n_heads, n_groups, n_splits;
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kTile * kLdsRow];
+  __shared__ uint32_t s_src[kTile];
+  __shared__ uint32_t s_rot[kTile];
+  __shared__ float s_ml[4][16][2];
+
+  // Workgroups of the same (sequence, split) but different head groups get
+  // the same x % 8, i.e. the same XCD and L2, and consecutive slots there.
+  const uint32_t x = blockIdx.x, xcd = x & 7, slot = x >> 3;
+  const uint32_t g = slot % a.n_groups;
+  const uint32_t bs = (slot / a.n_groups) * 8 + xcd;
+  if (bs >= a.n_seq * a.n_splits) return;
+  const uint32_t b = bs / a.n_splits, sp = bs % a.n_splits;
+
+  const uint32_t base = a.im.seq_base[b];
+  const uint32_t N = a.im.seq_base[b + 1] - base;
+  const uint32_t per = ((N + a.n_splits - 1) / a.n_splits + kTile - 1) / kTile * kTile;
+  const uint32_t r0 = min(N, sp * per), r1 = min(N, r0 + per);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hq = lane >> 4, hr = lane & 15;
+  const uint32_t head = g * 16 + hr;
+
+  bf16x8_t qb[18];
+  load_q(a.q_lat, a.q_rope, b, a.n_heads, head, qb);
+
+  f32x4_t o[32];
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  const uint32_t ntiles = (r1 - r0 + kTile - 1) / kTile;
+  uint4 v[kUnitsPerThread];
+  if (ntiles > 0) {
+    tile_row_info(a.im, base + r0, min((uint32_t)kTile, r1 - r0), s_src, s_rot);
+    __syncthreads();
+    load_tile(a.pool, s_src, min((uint32_t)kTile, r1 - r0), v);
+  }
+  for (uint32_t t = 0; t < ntiles; ++t) {
+    const uint32_t t0 = r0 + t * kTile;
+    const uint32_t nrows = min((uint32_t)kTile, r1 - t0);
+    rotate_tile_regs(a.im.trig, s_rot, v);
+    __syncthreads();  // previous tile fully consumed, row info of this tile no longer needed
+    store_tile_lds(s_tile, v);
+    if (t + 1 < ntiles) {
+      const uint32_t n1 = min((uint32_t)kTile, r1 - (t0 + kTile));
+      tile_row_info(a.im, base + t0 + kTile, n1, s_src, s_rot);
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(a.pool, s_src, min((uint32_t)kTile, r1 - (t0 + kTile)), v);
+
+    // this wave: tile rows [16 wave, 16 wave + 16)
+    const int row0 = 16 * wave;
+    if ((uint32_t)row0 < nrows) {
+      const f32x4_t acc = qk_block(s_tile, row0, qb);
+      float s[1][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[0][i] = ((uint32_t)(row0 + 4 * hq + i) < nrows) ? acc[i] * a.scale_log2 : -INFINITY;
+      i16x4_t pb[1];
+      softmax_update<1>(s, m, l, o, pb);
+      pv_block(s_tile, row0, pb[0], o);
+    }
+  }
+
+  // merge the 4 waves: sum l over the 4 lanes of each head, then combine
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (hq == 0) {
+    s_ml[wave][hr][0] = m;
+    s_ml[wave][hr][1] = l;
+  }
+  __syncthreads();
+  float mstar = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) mstar = fmaxf(mstar, s_ml[w][hr][0]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = s_ml[w][hr][0];
+    if (mw != -INFINITY) lsum += s_ml[w][hr][1] * exp2f(mw - mstar);
+  }
+  const float f = (m == -INFINITY) ? 0.f : exp2f(m - mstar);
+  float* red = reinterpret_cast<float*>(s_tile);  // [16 heads][512]
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) {
+        float4* dst = reinterpret_cast<float4*>(red + hr * IRM_D_LATENT + 16 * nb + 4 * hq);
+        float4 cur = (w == 0) ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
+        cur.x += f * o[nb][0];
+        cur.y += f * o[nb][1];
+        cur.z += f * o[nb][2];
+        cur.w += f * o[nb][3];
+        *dst = cur;
+      }
+    }
+    __syncthreads();
+  }
+  // write the partial of this (sequence, split, head group)
+  const size_t pidx = ((size_t)b * a.n_splits + sp) * a.n_heads + g * 16;
+  const float4* src = reinterpret_cast<const float4*>(red);
+  float4* dst = reinterpret_cast<float4*>(a.ws_acc + pidx * IRM_D_LATENT);
+  for (int i = threadIdx.x; i < 16 * IRM_D_LATENT / 4; i += kThreads) dst[i] = src[i];
+  if (threadIdx.x < 16) {
+    a.ws_ml[(pidx + threadIdx.x) * 2 + 0] = mstar;
+    a.ws_ml[(pidx + threadIdx.x) * 2 + 1] = (mstar == -INFINITY) ? 0.f : lsum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split-KV decode, pass 2: merge the splits of each (sequence, head)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws_acc,
+                                                             const float* __restrict__ ws_ml,
+                                                             uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse,
+                                                             uint32_t n_heads, uint32_t n_splits) {
+  const uint32_t bh = blockIdx.x;
+  const uint32_t b = bh / n_heads, h = bh % n_heads;
+  float mx = -INFINITY;
+  for (uint32_t s = 0; s < n_splits; ++s)
+    mx = fmaxf(mx, ws_ml[(((size_t)b * n_splits + s) * n_heads + h) * 2]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (uint32_t s = 0; s < n_splits; ++s) {
+    const size_t p = ((size_t)b * n_splits + s) * n_heads + h;
+    const float ms = ws_ml[p * 2];
+    if (ms == -INFINITY) continue;
+    const float f = exp2f(ms - mx);
+    L += f * ws_ml[p * 2 + 1];
+    const float4 v = reinterpret_cast<const float4*>(ws_acc + p * IRM_D_LATENT)[threadIdx.x];
+    acc.x += f * v.x;
+    acc.y += f * v.y;
+    acc.z += f * v.z;
+    acc.w += f * v.w;
+  }
+  const float inv = 1.f / L;
+  uint2 w;
+  w.x = pack_bf16(acc.x * inv, acc.y * inv);
+  w.y = pack_bf16(acc.z * inv, acc.w * inv);
+  reinterpret_cast<uint2*>(out + (size_t)bh * IRM_D_LATENT)[threadIdx.x] = w;
+  if (lse && threadIdx.x == 0) lse[bh] = (mx + log2f(L)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// chunked tail-prefill: 4 queries per workgroup (one per wave), 16 heads
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+  Image im;
+  const uint4* pool;
+  const uint4* q_lat;
+  const uint4* q_rope;
+  uint16_t* out;
+  float* lse;
+  uint32_t n_q, n_heads, n_groups;
+  int32_t q_pos0;
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kTile * kLdsRow];
+  __shared__ uint32_t s_src[kTile];
+  __shared__ uint32_t s_rot[kTile];
+
+  const uint32_t g = blockIdx.x % a.n_groups;
+  const uint32_t qblk = blockIdx.x / a.n_groups;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hq = lane >> 4, hr = lane & 15;
+  const uint32_t head = g * 16 + hr;
+  const uint32_t qi = qblk * 4 + wave;
+  const bool active = qi < a.n_q;
+  const uint32_t q_last = min(a.n_q, qblk * 4 + 4) - 1;
+  const uint32_t rows = (uint32_t)a.q_pos0 + q_last + 1;   // KV rows this workgroup visits
+  const int64_t lim = active ? (int64_t)a.q_pos0 + qi : -1;  // last visible row of this wave
+  const uint32_t base = a.im.seq_base[0];
+
+  bf16x8_t qb[18];
+  load_q(a.q_lat, a.q_rope, active ? qi : q_last, a.n_heads, head, qb);
+  f32x4_t o[32];
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  const uint32_t ntiles = (rows + kTile - 1) / kTile;
+  uint4 v[kUnitsPerThread];
+  tile_row_info(a.im, base, min((uint32_t)kTile, rows), s_src, s_rot);
+  __syncthreads();
+  load_tile(a.pool, s_src, min((uint32_t)kTile, rows), v);
+  for (uint32_t t = 0; t < ntiles; ++t) {
+    const uint32_t t0 = t * kTile;
+    rotate_tile_regs(a.im.trig, s_rot, v);
+    __syncthreads();
+    store_tile_lds(s_tile, v);
+    if (t + 1 < ntiles) tile_row_info(a.im, base + t0 + kTile, min((uint32_t)kTile, rows - t0 - kTile), s_src, s_rot);
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(a.pool, s_src, min((uint32_t)kTile, rows - t0 - kTile), v);
+
+    if ((int64_t)t0 <= lim) {
+      f32x4_t acc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((int64_t)(t0 + 16 * j) <= lim) acc[j] = qk_block(s_tile, 16 * j, qb);
+        else acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      float s[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[j][i] = ((int64_t)(t0 + 16 * j + 4 * hq + i) <= lim) ? acc[j][i] * a.scale_log2 : -INFINITY;
+      i16x4_t pb[4];
+      softmax_update<4>(s, m, l, o, pb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((int64_t)(t0 + 16 * j) <= lim) pv_block(s_tile, 16 * j, pb[j], o);
+    }
+  }
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!active) return;
+  const float inv = 1.f / l;
+  uint16_t* op = a.out + ((size_t)qi * a.n_heads + head) * IRM_D_LATENT + 4 * hq;
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) {
+    uint2 w;
+    w.x = pack_bf16(o[nb][0] * inv, o[nb][1] * inv);
+    w.y = pack_bf16(o[nb][2] * inv, o[nb][3] * inv);
+    *reinterpret_cast<uint2*>(op + 16 * nb) = w;
+  }
+  if (a.lse && hq == 0) a.lse[(size_t)qi * a.n_heads + head] = (m + log2f(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+irm_status hip_check(hipError_t err, const char* what) {
+  if (err == hipSuccess) return IRM_OK;
+  return fail(IRM_EHIP, std::string(what) + ": " + hipGetErrorString(err));
+}
+
+irm_status launch_check(const char* what) { return hip_check(hipGetLastError(), what); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The kernels are built for gfx950 only; refuse other devices up front.
+irm_status check_device() {
+  static thread_local int checked_dev = -1;
+  int dev = 0;
+  irm_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st != IRM_OK) return st;
+  if (dev == checked_dev) return IRM_OK;
+  hipDeviceProp_t prop;
+  st = hip_check(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
+  if (st != IRM_OK) return st;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(IRM_EUNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", kernels are built for gfx950");
+  checked_dev = dev;
+  return IRM_OK;
+}
+
+irm_status need_uploaded(const irm_table* t, const char* fn) {
+  if (!t) return fail(IRM_EINVAL, std::string(fn) + ": table is NULL");
+  if (!t->dev) return fail(IRM_EINVAL, std::string(fn) + ": table has not been uploaded");
+  return IRM_OK;
+}
+
+irm_status check_pool(const irm_table* t, const void* pool, uint64_t pool_rows, const char* fn) {
+  if (t->n_chunks && !pool) return fail(IRM_EINVAL, std::string(fn) + ": pool is NULL");
+  if (!aligned16(pool)) return fail(IRM_EINVAL, std::string(fn) + ": pool must be 16-byte aligned");
+  if (pool_rows < t->pool_rows)
+    return fail(IRM_ERANGE, std::string(fn) + ": pool has fewer rows than the table was built for");
+  return IRM_OK;
+}
+
+uint32_t default_splits(const irm_table* t, uint32_t n_groups) {
+  // aim for >= 2 workgroups per CU (256 CUs) with >= 256 rows per split
+  const uint32_t want = (512 + t->n_seq * n_groups - 1) / (t->n_seq * n_groups);
+  const uint32_t cap = (t->max_seq_len + 255) / 256;
+  uint32_t s = want < cap ? want : cap;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return s;
+}
+
+irm_status check_heads(uint32_t n_heads, const char* fn) {
+  if (n_heads == 0 || n_heads % 16 != 0 || n_heads > IRM_MAX_HEADS)
+    return fail(IRM_EUNSUPPORTED, std::string(fn) + ": n_heads must be a multiple of 16, at most 128");
+  return IRM_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" irm_status irm_table_upload(irm_table* t, const double* inv_freq, void* dev_buf,
+                                       size_t dev_bytes, void* stream) {
+  if (!t) return fail(IRM_EINVAL, "irm_table_upload: table is NULL");
+  if (!inv_freq) return fail(IRM_EINVAL, "irm_table_upload: inv_freq is NULL");
+  if (!dev_buf) return fail(IRM_EINVAL, "irm_table_upload: dev_buf is NULL");
+  if (reinterpret_cast<uintptr_t>(dev_buf) % irm::kAlign)
+    return fail(IRM_EINVAL, "irm_table_upload: dev_buf must be 256-byte aligned");
+  if (dev_bytes < t->layout.bytes)
+    return fail(IRM_EWORKSPACE, "irm_table_upload: dev_buf smaller than the device image");
+  for (int i = 0; i < (int)irm::kPairs; ++i)
+    if (!std::isfinite(inv_freq[i])) return fail(IRM_EINVAL, "irm_table_upload: inv_freq not finite");
+  irm_status st = check_device();
+  if (st != IRM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_check(hipMemcpyAsync(dev_buf, t->image.data(), t->layout.off_trig, hipMemcpyHostToDevice, s),
+                 "irm_table_upload: hipMemcpyAsync");
+  if (st != IRM_OK) return st;
+  t->dev = dev_buf;
+  st = irm_table_set_rope(t, inv_freq, stream);
+  if (st != IRM_OK) t->dev = nullptr;
+  return st;
+}
+
+extern "C" irm_status irm_table_set_rope(irm_table* t, const double* inv_freq, void* stream) {
+  irm_status st = need_uploaded(t, "irm_table_set_rope");
+  if (st != IRM_OK) return st;
+  if (!inv_freq) return fail(IRM_EINVAL, "irm_table_set_rope: inv_freq is NULL");
+  for (int i = 0; i < (int)irm::kPairs; ++i)
+    if (!std::isfinite(inv_freq[i])) return fail(IRM_EINVAL, "irm_table_set_rope: inv_freq not finite");
+  if (!t->n_chunks) return IRM_OK;
+  InvFreq f;
+  std::memcpy(f.w, inv_freq, sizeof(f.w));
+  const uint32_t n = t->n_chunks * irm::kPairs;
+  const Image im = image_of(t);
+  hipLaunchKernelGGL(trig_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     im.ents, t->n_chunks, f, const_cast<float2*>(im.trig));
+  return launch_check("irm_table_set_rope: trig kernel");
+}
+
+extern "C" irm_status irm_table_gather_index(const irm_table* t, int64_t* pool_row, int32_t* delta,
+                                             void* stream) {
+  irm_status st = need_uploaded(t, "irm_table_gather_index");
+  if (st != IRM_OK) return st;
+  if (t->total_rows == 0 || (!pool_row && !delta)) return IRM_OK;
+  const uint32_t n = (uint32_t)t->total_rows;
+  hipLaunchKernelGGL(gather_index_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), image_of(t), n, pool_row, delta);
+  return launch_check("irm_table_gather_index");
+}
+
+extern "C" irm_status irm_rotate_gather(const irm_table* t, const void* pool, uint64_t pool_rows,
+                                        void* out_kv, float* kr_f32, void* stream) {
+  irm_status st = need_uploaded(t, "irm_rotate_gather");
+  if (st != IRM_OK) return st;
+  if (t->total_rows == 0) return IRM_OK;
+  if ((st = check_pool(t, pool, pool_rows, "irm_rotate_gather")) != IRM_OK) return st;
+  if (!out_kv || !aligned16(out_kv)) return fail(IRM_EINVAL, "irm_rotate_gather: out_kv NULL or misaligned");
+  if (kr_f32 && !aligned16(kr_f32)) return fail(IRM_EINVAL, "irm_rotate_gather: kr_f32 misaligned");
+  const uint32_t n = (uint32_t)t->total_rows;
+  hipLaunchKernelGGL(rotate_gather_kernel, dim3((n + kTile - 1) / kTile), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), image_of(t), n,
+                     static_cast<const uint4*>(pool), static_cast<uint4*>(out_kv), kr_f32);
+  return launch_check("irm_rotate_gather");
+}
+
+extern "C" irm_status irm_mla_decode_workspace(const irm_table* t, uint32_t n_heads, uint32_t n_splits,
+                                               size_t* bytes) {
+  if (!t || !bytes) return fail(IRM_EINVAL, "irm_mla_decode_workspace: NULL argument");
+  irm_status st = check_heads(n_heads, "irm_mla_decode_workspace");
+  if (st != IRM_OK) return st;
+  const uint32_t S = n_splits ? n_splits : default_splits(t, n_heads / 16);
+  const size_t parts = (size_t)t->n_seq * S * n_heads;
+  *bytes = irm::align_up(parts * IRM_D_LATENT * sizeof(float)) + irm::align_up(parts * 2 * sizeof(float));
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_mla_decode(const void* q_latent, const void* q_rope, const irm_table* t,
+                                     const void* pool, uint64_t pool_rows, uint32_t n_heads,
+                                     uint32_t n_splits, float scale, void* out, float* lse,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+  irm_status st = need_uploaded(t, "irm_mla_decode");
+  if (st != IRM_OK) return st;
+  if ((st = check_heads(n_heads, "irm_mla_decode")) != IRM_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(IRM_EINVAL, "irm_mla_decode: scale must be finite and > 0");
+  if (t->n_seq == 0) return IRM_OK;
+  if (t->min_seq_len == 0) return fail(IRM_EINVAL, "irm_mla_decode: every sequence needs at least one row");
+  if ((st = check_pool(t, pool, pool_rows, "irm_mla_decode")) != IRM_OK) return st;
+  if (!q_latent || !q_rope || !out || !aligned16(q_latent) || !aligned16(q_rope) || !aligned16(out))
+    return fail(IRM_EINVAL, "irm_mla_decode: q_latent, q_rope and out must be non-NULL and 16-byte aligned");
+  if (n_splits > 4096) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: n_splits above 4096");
+  const uint32_t G = n_heads / 16;
+  const uint32_t S = n_splits ? n_splits : default_splits(t, G);
+  size_t need = 0;
+  irm_mla_decode_workspace(t, n_heads, S, &need);
+  if (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % irm::kAlign)
+    return fail(IRM_EWORKSPACE, "irm_mla_decode: workspace missing, misaligned or smaller than "
+                                "irm_mla_decode_workspace");
+  const size_t parts = (size_t)t->n_seq * S * n_heads;
+  if ((st = check_device()) != IRM_OK) return st;
+  DecodeArgs a;
+  a.im = image_of(t);
+  a.pool = static_cast<const uint4*>(pool);
+  a.q_lat = static_cast<const uint4*>(q_latent);
+  a.q_rope = static_cast<const uint4*>(q_rope);
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                     irm::align_up(parts * IRM_D_LATENT * sizeof(float)));
+  a.n_seq = t->n_seq;
+  a.n_heads = n_heads;
+  a.n_groups = G;
+  a.n_splits = S;
+  a.scale_log2 = scale * kLog2e;
+  const uint64_t bs = (uint64_t)t->n_seq * S;
+  const uint64_t grid = (bs + 7) / 8 * 8 * G;
+  if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(decode_split_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+  if ((st = launch_check("irm_mla_decode: split kernel")) != IRM_OK) return st;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(t->n_seq * n_heads), dim3(128), 0, s, a.ws_acc, a.ws_ml,
+                     static_cast<uint16_t*>(out), lse, n_heads, S);
+  return launch_check("irm_mla_decode: combine kernel");
+}
+
+extern "C" irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_rope, int32_t q_pos0,
+                                           uint32_t n_q, const irm_table* t, const void* pool,
+                                           uint64_t pool_rows, uint32_t n_heads, float scale,
+                                           void* out, float* lse, void* stream) {
+  irm_status st = need_uploaded(t, "irm_mla_prefill_tail");
+  if (st != IRM_OK) return st;
+  if ((st = check_heads(n_heads, "irm_mla_prefill_tail")) != IRM_OK) return st;
+  if (t->n_seq != 1) return fail(IRM_EINVAL, "irm_mla_prefill_tail: table must hold exactly one sequence");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(IRM_EINVAL, "irm_mla_prefill_tail: scale must be finite and > 0");
+  if (q_pos0 < 0 || n_q == 0 || (uint64_t)q_pos0 + n_q > t->total_rows)
+    return fail(IRM_ERANGE, "irm_mla_prefill_tail: queries must satisfy 0 <= q_pos0, 1 <= n_q, q_pos0 + n_q <= N");
+  if ((st = check_pool(t, pool, pool_rows, "irm_mla_prefill_tail")) != IRM_OK) return st;
+  if (!q_latent || !q_rope || !out || !aligned16(q_latent) || !aligned16(q_rope) || !aligned16(out))
+    return fail(IRM_EINVAL, "irm_mla_prefill_tail: q_latent, q_rope and out must be non-NULL and 16-byte aligned");
+  if ((st = check_device()) != IRM_OK) return st;
+  PrefillArgs a;
+  a.im = image_of(t);
+  a.pool = static_cast<const uint4*>(pool);
+  a.q_lat = static_cast<const uint4*>(q_latent);
+  a.q_rope = static_cast<const uint4*>(q_rope);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.n_q = n_q;
+  a.n_heads = n_heads;
+  a.n_groups = n_heads / 16;
+  a.q_pos0 = q_pos0;
+  a.scale_log2 = scale * kLog2e;
+  const uint64_t grid = (uint64_t)(n_q + 3) / 4 * a.n_groups;
+  if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_prefill_tail: grid too large");
+  hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+  return launch_check("irm_mla_prefill_tail");
+}

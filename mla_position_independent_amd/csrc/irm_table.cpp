@@ -1,0 +1,200 @@
+// Host side of the chunk table: validation, device-image packing, host
+// expansion and the RoPE frequency helper.  No HIP call is made here, so
+// everything in this file runs on a machine without a GPU.
+//
+// The table encodes the serve-path assembly of the Irminsul pages
+// (gentlecold.top article, section 5): segments are appended in target
+// order, each registry hit placed at p_tgt moves every one of its tokens by
+// the same delta = p_tgt - p_src (section 15 worked example), and positions
+// below 32 are always fresh (gist.science summary section 2.2; gentlecold.top
+// section 7).
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "irm_internal.h"
+
+namespace irm {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+irm_status fail(irm_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+}  // namespace irm
+
+using irm::fail;
+
+extern "C" const char* irm_last_error(void) { return irm::g_last_error.c_str(); }
+
+extern "C" irm_status irm_rope_inv_freq(double theta, double* inv_freq) {
+  if (!inv_freq) return fail(IRM_EINVAL, "irm_rope_inv_freq: inv_freq is NULL");
+  if (!(theta > 1.0) || !std::isfinite(theta))
+    return fail(IRM_EINVAL, "irm_rope_inv_freq: theta must be finite and > 1");
+  for (int i = 0; i < (int)irm::kPairs; ++i)
+    inv_freq[i] = std::pow(theta, -2.0 * (double)i / (double)IRM_D_ROPE);
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunks,
+                                       const uint32_t* seq_first, uint32_t n_seq,
+                                       uint64_t pool_rows, irm_table** out) {
+  if (!out) return fail(IRM_EINVAL, "irm_table_create: out is NULL");
+  *out = nullptr;
+  if (!seq_first) return fail(IRM_EINVAL, "irm_table_create: seq_first is NULL");
+  if (n_chunks > 0 && !chunks) return fail(IRM_EINVAL, "irm_table_create: chunks is NULL");
+  if (seq_first[0] != 0 || seq_first[n_seq] != n_chunks)
+    return fail(IRM_EINVAL, "irm_table_create: seq_first must run from 0 to n_chunks");
+  for (uint32_t s = 0; s < n_seq; ++s)
+    if (seq_first[s + 1] < seq_first[s])
+      return fail(IRM_EINVAL, "irm_table_create: seq_first must be nondecreasing");
+
+  // kernels index pool rows with 32 bits; a larger pool cannot be addressed
+  if (pool_rows > 0x100000000ull) pool_rows = 0x100000000ull;
+
+  irm_table* t = new (std::nothrow) irm_table();
+  if (!t) return fail(IRM_EINVAL, "irm_table_create: out of host memory");
+  t->n_seq = n_seq;
+  t->n_chunks = n_chunks;
+  t->pool_rows = pool_rows;
+  t->entries.resize(n_chunks);
+  t->seq_first.assign(seq_first, seq_first + n_seq + 1);
+  t->seq_base.assign((size_t)n_seq + 1, 0);
+
+  const int64_t kI32Max = 2147483647LL, kI32Min = -2147483648LL;
+  uint64_t total = 0;
+  uint32_t max_len = 0, min_len = n_seq ? 0xffffffffu : 0;
+  for (uint32_t s = 0; s < n_seq; ++s) {
+    int64_t expect = 0;
+    t->seq_base[s] = (uint32_t)total;
+    for (uint32_t e = seq_first[s]; e < seq_first[s + 1]; ++e) {
+      const irm_chunk& c = chunks[e];
+      std::string where = "entry " + std::to_string(e) + " (sequence " + std::to_string(s) + ")";
+      if (c.flags & ~IRM_FRESH) { delete t; return fail(IRM_EINVAL, where + ": unknown flag bits"); }
+      if (c.len == 0) { delete t; return fail(IRM_EINVAL, where + ": zero length"); }
+      if ((uint64_t)c.pool_row + c.len > pool_rows) {
+        delete t;
+        return fail(IRM_ERANGE, where + ": pool rows [" + std::to_string(c.pool_row) + ", +" +
+                                    std::to_string(c.len) + ") exceed the pool");
+      }
+      if ((int64_t)c.p_tgt != expect) {
+        delete t;
+        return fail(IRM_ELAYOUT, where + ": p_tgt " + std::to_string(c.p_tgt) + " should be " +
+                                     std::to_string(expect));
+      }
+      if ((int64_t)c.p_tgt + (int64_t)c.len - 1 > kI32Max) {
+        delete t;
+        return fail(IRM_ERANGE, where + ": positions exceed int32");
+      }
+      const bool fresh = (c.flags & IRM_FRESH) != 0;
+      if (fresh && c.p_src != c.p_tgt) {
+        delete t;
+        return fail(IRM_EINVAL, where + ": fresh entry needs p_src == p_tgt");
+      }
+      if (!fresh && c.p_tgt < IRM_CARVE_OUT) {
+        delete t;
+        return fail(IRM_ECARVEOUT, where + ": registry rows below position 32 must be fresh");
+      }
+      const int64_t delta = (int64_t)c.p_tgt - (int64_t)c.p_src;
+      if (delta > kI32Max || delta < kI32Min) {
+        delete t;
+        return fail(IRM_ERANGE, where + ": delta exceeds int32");
+      }
+      irm::DevEntry& d = t->entries[e];
+      d.pool_row = c.pool_row;
+      d.len = c.len;
+      d.p_src = c.p_src;
+      d.p_tgt = c.p_tgt;
+      d.flags = c.flags;
+      d.seq = s;
+      d.out_row = (uint32_t)(total + (uint64_t)c.p_tgt);
+      d.delta = fresh ? 0 : (int32_t)delta;
+      expect = (int64_t)c.p_tgt + c.len;
+    }
+    total += (uint64_t)expect;
+    if (total > (uint64_t)kI32Max) {
+      delete t;
+      return fail(IRM_ERANGE, "irm_table_create: total assembled rows exceed int32");
+    }
+    if ((uint32_t)expect > max_len) max_len = (uint32_t)expect;
+    if ((uint32_t)expect < min_len) min_len = (uint32_t)expect;
+  }
+  t->seq_base[n_seq] = (uint32_t)total;
+  t->total_rows = total;
+  t->max_seq_len = max_len;
+  t->min_seq_len = min_len;
+
+  // block map: entry holding assembled row b * kBlockRows
+  t->n_blocks = (uint32_t)((total + irm::kBlockRows - 1) / irm::kBlockRows);
+  t->block_map.assign(t->n_blocks ? t->n_blocks : 1, 0);
+  {
+    uint32_t e = 0;
+    for (uint32_t b = 0; b < t->n_blocks; ++b) {
+      uint64_t row = (uint64_t)b * irm::kBlockRows;
+      while ((uint64_t)t->entries[e].out_row + t->entries[e].len <= row) ++e;
+      t->block_map[b] = e;
+    }
+  }
+
+  // image layout and host image
+  irm::ImageLayout& L = t->layout;
+  size_t off = 0;
+  L.off_entries = off;   off = irm::align_up(off + sizeof(irm::DevEntry) * (size_t)n_chunks);
+  L.off_seq_first = off; off = irm::align_up(off + sizeof(uint32_t) * ((size_t)n_seq + 1));
+  L.off_seq_base = off;  off = irm::align_up(off + sizeof(uint32_t) * ((size_t)n_seq + 1));
+  L.off_block_map = off; off = irm::align_up(off + sizeof(uint32_t) * t->block_map.size());
+  L.off_trig = off;      off = irm::align_up(off + sizeof(float) * 2 * irm::kPairs * (size_t)n_chunks);
+  L.bytes = off;
+  t->image.assign(L.off_trig, 0);
+  if (n_chunks)
+    std::memcpy(t->image.data() + L.off_entries, t->entries.data(), sizeof(irm::DevEntry) * n_chunks);
+  std::memcpy(t->image.data() + L.off_seq_first, t->seq_first.data(), sizeof(uint32_t) * (n_seq + 1));
+  std::memcpy(t->image.data() + L.off_seq_base, t->seq_base.data(), sizeof(uint32_t) * (n_seq + 1));
+  std::memcpy(t->image.data() + L.off_block_map, t->block_map.data(),
+              sizeof(uint32_t) * t->block_map.size());
+  *out = t;
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_table_destroy(irm_table* t) {
+  delete t;
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_table_info(const irm_table* t, uint32_t* n_seq, uint32_t* n_chunks,
+                                     uint64_t* total_rows, uint32_t* max_seq_len,
+                                     size_t* device_bytes) {
+  if (!t) return fail(IRM_EINVAL, "irm_table_info: table is NULL");
+  if (n_seq) *n_seq = t->n_seq;
+  if (n_chunks) *n_chunks = t->n_chunks;
+  if (total_rows) *total_rows = t->total_rows;
+  if (max_seq_len) *max_seq_len = t->max_seq_len;
+  if (device_bytes) *device_bytes = t->layout.bytes;
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_table_seq_base(const irm_table* t, uint64_t* seq_base) {
+  if (!t || !seq_base) return fail(IRM_EINVAL, "irm_table_seq_base: NULL argument");
+  for (uint32_t s = 0; s <= t->n_seq; ++s) seq_base[s] = t->seq_base[s];
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_table_expand_host(const irm_table* t, int64_t* pool_row, int32_t* delta,
+                                            uint8_t* fresh) {
+  if (!t) return fail(IRM_EINVAL, "irm_table_expand_host: table is NULL");
+  for (const irm::DevEntry& d : t->entries) {
+    for (uint32_t j = 0; j < d.len; ++j) {
+      const uint64_t r = (uint64_t)d.out_row + j;
+      if (pool_row) pool_row[r] = (int64_t)d.pool_row + j;
+      if (delta) delta[r] = d.delta;
+      if (fresh) fresh[r] = (d.flags & IRM_FRESH) ? 1 : 0;
+    }
+  }
+  return IRM_OK;
+}

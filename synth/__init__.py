@@ -16,5 +16,10 @@ from .workloads import (  # noqa: F401
     make_workload,
     WORKLOADS,
     random_table,
+    tiny_decode,
+    rotate_gather_batch,
+    batched_decode,
+    long_decode,
+    tail_prefill,
     manifest,
 )

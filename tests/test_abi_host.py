@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+symbol the header declares, and the chunk-table builder agrees bit for bit
+with the oracle's table expansion, including every failure code."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_position_independent_amd as irm
+import oracle
+from synth import CHUNK_DTYPE, FRESH, random_table, tiny_decode, batched_decode, tail_prefill
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "irm.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(irm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = irm.lib()
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(irm.EXPORTS) == names
+
+
+def test_rope_inv_freq_matches_oracle():
+    got = irm.rope_inv_freq(10000.0)
+    want = oracle.rope_inv_freq(10000.0)
+    assert np.allclose(got, want, rtol=1e-15, atol=0)   # a few ulp between libm pow and numpy power
+    with pytest.raises(irm.IrmError) as e:
+        irm.rope_inv_freq(0.5)
+    assert e.value.code == "EINVAL"
+
+
+def _compare_with_oracle(chunks, seq_first, pool_rows):
+    t = irm.Table(chunks, seq_first, pool_rows)
+    pr, de, fr = t.expand_host()
+    ref = oracle.expand_table(chunks, seq_first, pool_rows)
+    base = t.seq_base()
+    assert base[0] == 0
+    for s, (g, d, f) in enumerate(ref):
+        sl = slice(int(base[s]), int(base[s + 1]))
+        assert np.array_equal(pr[sl], g)
+        assert np.array_equal(de[sl].astype(np.int64), d)
+        assert np.array_equal(fr[sl].astype(bool), f)
+    assert t.total_rows == sum(len(g) for g, _, _ in ref)
+    assert t.n_seq == len(ref)
+    assert t.max_seq_len == max([len(g) for g, _, _ in ref], default=0)
+    return t
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_table_matches_oracle_random(seed):
+    rng = np.random.default_rng(500 + seed)
+    n_seq = int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.integers(1, 700, size=n_seq)]
+    w = random_table(seed, lens, p_hit=0.7, prefix_frac=float(rng.random()) * 0.5,
+                     len_fn=lambda r: int(r.integers(1, 80)))
+    _compare_with_oracle(w.chunks, w.seq_first, w.pool.shape[0])
+
+
+def test_table_matches_oracle_workloads():
+    for w in (tiny_decode(), batched_decode(batch=3, ctx=3000), tail_prefill(n_q=64, prefix_end=1000,
+                                                                           hits_end=4000, total=6000)):
+        _compare_with_oracle(w.chunks, w.seq_first, w.pool.shape[0])
+
+
+def test_table_empty_sequences():
+    t = _compare_with_oracle(np.zeros(0, CHUNK_DTYPE), np.array([0, 0, 0], np.uint32), 0)
+    assert t.total_rows == 0 and t.n_seq == 2
+    c = np.array([(0, 40, 0, 0, FRESH)], dtype=CHUNK_DTYPE)
+    _compare_with_oracle(c, np.array([0, 0, 1, 1], np.uint32), 40)
+
+
+CASES = [
+    ([(0, 32, 0, 0, FRESH | 4)], "EINVAL"),
+    ([(0, 0, 0, 0, FRESH)], "EINVAL"),
+    ([(990, 32, 0, 0, FRESH)], "ERANGE"),
+    ([(0, 32, 5, 5, FRESH)], "ELAYOUT"),
+    ([(0, 32, 0, 0, FRESH), (40, 8, 7, 33, 0)], "ELAYOUT"),
+    ([(0, 32, 3, 0, FRESH)], "EINVAL"),
+    ([(0, 16, 0, 0, FRESH), (40, 8, 500, 16, 0)], "ECARVEOUT"),
+    ([(0, 32, 0, 0, FRESH), (40, 8, -2**31, 32, 0)], "ERANGE"),
+    ([(0, 32, 0, 0, FRESH), (40, 8, 2**31 - 1, 32, 0)], "OK"),
+    ([(0, 31, 0, 0, FRESH), (40, 8, 31, 31, 0)], "ECARVEOUT"),   # exact prefix below 32 still rejected
+]
+
+
+@pytest.mark.parametrize("rows,code", CASES)
+def test_table_error_codes_match_oracle(rows, code):
+    c = np.array(rows, dtype=CHUNK_DTYPE)
+    sf = np.array([0, len(rows)], dtype=np.uint32)
+    try:
+        oracle.expand_table(c, sf, 1000)
+        ocode = "OK"
+    except oracle.TableError as e:
+        ocode = e.code
+    assert ocode == code
+    if code == "OK":
+        _compare_with_oracle(c, sf, 1000)
+    else:
+        with pytest.raises(irm.IrmError) as e:
+            irm.Table(c, sf, 1000)
+        assert e.value.code == code
+        assert len(str(e.value)) > 20
+
+
+def test_bad_seq_first():
+    c = np.array([(0, 32, 0, 0, FRESH)], dtype=CHUNK_DTYPE)
+    for sf in ([1, 1], [0, 2], [0, 1, 0, 1]):
+        with pytest.raises(irm.IrmError) as e:
+            irm.Table(c, np.array(sf, np.uint32), 1000)
+        assert e.value.code == "EINVAL"
+
+
+def test_seq_base_is_prefix_sum():
+    w = random_table(3, [100, 1, 257, 64])
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0])
+    assert t.seq_base().tolist() == [0, 100, 101, 358, 422]
+    assert t.device_bytes % 256 == 0 and t.device_bytes >= 32 * t.n_chunks + 256 * t.n_chunks

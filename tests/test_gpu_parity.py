@@ -1,0 +1,354 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (derived in the design doc):
+* gather indices and deltas, c_KV bytes, and fresh / delta-0 k_r bytes: bit-exact;
+* rotated k_r (float side output): relative L2 <= 1e-5; bf16 k_r within one
+  bf16 ulp of the oracle's exact value;
+* attention output (bf16): relative L2 <= 5e-3 per tensor; lse within 5e-3
+  absolute.  The kernels round the rotated k_r to bf16 before the score
+  product (as the stored cache would be), which moves each score by at most
+  scale * 2^-9 * |q_rope| |k_r| (about 9e-3 for N(0,1) data, typically 1e-3);
+  lse is a softmax-weighted mean of those score errors.
+Full-size workloads are compared on sampled outputs the oracle computes one
+by one.
+"""
+import numpy as np
+import pytest
+
+import mla_position_independent_amd as irm
+import oracle
+from synth import (CHUNK_DTYPE, FRESH, random_table, tiny_decode, rotate_gather_batch,
+                   batched_decode, long_decode, tail_prefill)
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 5e-3
+KR_TOL = 1e-5
+LSE_TOL = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    irm.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
+
+
+def _table(w, inv=None):
+    return irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(
+        irm.rope_inv_freq(w.theta) if inv is None else inv)
+
+
+def _bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-30)))
+    return np.exp2(e - 7)
+
+
+# ---------------------------------------------------------------- rotate-gather
+def _check_gather(w, out_bits, kr, rows=None):
+    """Compare assembled rows (all, or the given global rows) with the oracle."""
+    inv = oracle.rope_inv_freq(w.theta)
+    exp = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
+    gather = np.concatenate([g for g, _, _ in exp]) if exp else np.zeros(0, np.int64)
+    delta = np.concatenate([d for _, d, _ in exp]) if exp else np.zeros(0, np.int64)
+    if rows is None:
+        rows = np.arange(gather.shape[0])
+    g, d = gather[rows], delta[rows]
+    c_ref, k_ref = oracle.assemble_rows(w.pool, g, d, inv)
+    # c_KV bit for bit
+    assert np.array_equal(out_bits[:, :512], w.pool[g, :512])
+    # unrotated k_r bit for bit
+    same = d == 0
+    assert np.array_equal(out_bits[same, 512:], w.pool[g[same], 512:])
+    # rotated k_r: float side output and bf16 output
+    if kr is not None:
+        assert rel_l2(kr.astype(np.float64), k_ref) <= KR_TOL
+        assert np.array_equal(kr[same].astype(np.float64), k_ref[same])
+    got = oracle.bf16_to_f64(out_bits[:, 512:])
+    assert np.all(np.abs(got - k_ref) <= _bf16_ulp(k_ref) * 1.0000001)
+    return gather, delta
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rotate_gather_small(seed):
+    rng = np.random.default_rng(900 + seed)
+    lens = [int(x) for x in rng.integers(1, 1500, size=int(rng.integers(1, 6)))]
+    short = lambda r: int(r.integers(1, 70))
+    cdc = lambda r: int(r.integers(32, 513))
+    w = random_table(seed, lens, p_hit=0.7, prefix_frac=0.2, len_fn=short if seed % 2 else cdc)
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    out, kr = irm.rotate_gather(t, pool, kr_f32=True)
+    out2 = irm.rotate_gather(t, pool)
+    pr, de = t.gather_index()
+    _sync()
+    ob = irm.from_device_bf16(out)
+    gather, delta = _check_gather(w, ob, kr.cpu().numpy())
+    assert np.array_equal(ob, irm.from_device_bf16(out2))          # deterministic
+    assert np.array_equal(pr.cpu().numpy(), gather)                 # gather map bit-exact
+    assert np.array_equal(de.cpu().numpy().astype(np.int64), delta)
+
+
+def test_rotate_gather_edge_cases():
+    import torch
+    # one-row entries, a one-row sequence, an empty sequence and hits at extreme deltas
+    rows = [(0, 40, 0, 0, FRESH), (100, 1, 131072 + 40, 40, 0), (101, 1, -131031, 41, 0),
+            (102, 5, 42, 42, 0), (200, 1, 0, 0, FRESH), (300, 33, 2**31 - 1, 32, 0)]
+    chunks = np.array(rows[:4] + rows[4:5] + [(400, 32, 0, 0, FRESH)] + rows[5:], dtype=CHUNK_DTYPE)
+    seq_first = np.array([0, 4, 4, 5, 7], np.uint32)
+    rng = np.random.default_rng(5)
+    from synth import randn_bf16, Workload
+    w = Workload("edge", randn_bf16(rng, (512, 576)), chunks, seq_first)
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    out, kr = irm.rotate_gather(t, pool, kr_f32=True)
+    _sync()
+    _check_gather(w, irm.from_device_bf16(out), kr.cpu().numpy())
+    # an empty table is a no-op
+    e = irm.Table(np.zeros(0, CHUNK_DTYPE), np.array([0, 0], np.uint32), 0).upload()
+    o = irm.rotate_gather(e, pool, out=torch.empty((0, 576), dtype=torch.bfloat16, device="cuda"))
+    _sync()
+    assert o.shape[0] == 0
+
+
+def test_rotate_gather_custom_inv_freq():
+    """A model's own rotary table (here fp32-rounded frequencies) is honoured."""
+    w = random_table(77, [700, 300])
+    inv = oracle.rope_inv_freq(10000.0).astype(np.float32).astype(np.float64)
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w, inv)
+    out, kr = irm.rotate_gather(t, pool, kr_f32=True)
+    _sync()
+    exp = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
+    g = np.concatenate([x for x, _, _ in exp]); d = np.concatenate([x for _, x, _ in exp])
+    _, k_ref = oracle.assemble_rows(w.pool, g, d, inv)
+    assert rel_l2(kr.cpu().numpy().astype(np.float64), k_ref) <= KR_TOL
+
+
+def test_rotate_gather_full_size_sampled():
+    """64 requests x 32768 tokens over a 4096-chunk registry (the benchmarked
+    launch); gather map bit-exact everywhere, rows sampled against the oracle."""
+    w = rotate_gather_batch()
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    out, kr = irm.rotate_gather(t, pool, kr_f32=True)
+    pr, de = t.gather_index()
+    _sync()
+    exp = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
+    gather = np.concatenate([g for g, _, _ in exp]); delta = np.concatenate([d for _, d, _ in exp])
+    assert np.array_equal(pr.cpu().numpy(), gather)
+    assert np.array_equal(de.cpu().numpy().astype(np.int64), delta)
+    rng = np.random.default_rng(0)
+    rows = np.sort(np.concatenate([rng.choice(gather.shape[0], 16384, replace=False),
+                                   [0, 31, 32, gather.shape[0] - 1]]))
+    import torch
+    idx = torch.from_numpy(rows).cuda()
+    ob = irm.from_device_bf16(out.index_select(0, idx))
+    krs = kr.index_select(0, idx).cpu().numpy()
+    w_rows = np.arange(rows.shape[0])
+    # reuse the checker on the sampled rows
+    c_ref, k_ref = oracle.assemble_rows(w.pool, gather[rows], delta[rows], oracle.rope_inv_freq(w.theta))
+    assert np.array_equal(ob[:, :512], w.pool[gather[rows], :512])
+    same = delta[rows] == 0
+    assert np.array_equal(ob[same, 512:], w.pool[gather[rows][same], 512:])
+    assert rel_l2(krs.astype(np.float64), k_ref) <= KR_TOL
+    got = oracle.bf16_to_f64(ob[:, 512:])
+    assert np.all(np.abs(got - k_ref) <= _bf16_ulp(k_ref) * 1.0000001)
+    assert w_rows.shape[0] == rows.shape[0]
+
+
+# ---------------------------------------------------------------- decode
+def _oracle_decode(w, seqs, heads=None):
+    inv = oracle.rope_inv_freq(w.theta)
+    exp = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
+    outs, lses = [], []
+    for b in seqs:
+        g, d, _ = exp[b]
+        c, k = oracle.assemble_rows(w.pool, g, d, inv)
+        hs = np.arange(w.n_heads) if heads is None else np.asarray(heads)
+        o, l = oracle.mla_decode(oracle.bf16_to_f64(w.q_lat[b, hs]), oracle.bf16_to_f64(w.q_rope[b, hs]),
+                                 c, k, w.scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+def _gpu_decode(w, n_splits=0, table=None, pool=None):
+    pool = irm.to_device_bf16(w.pool) if pool is None else pool
+    t = _table(w) if table is None else table
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    out, lse = irm.mla_decode(ql, qr, t, pool, n_splits=n_splits, scale=w.scale, want_lse=True)
+    _sync()
+    return oracle.bf16_to_f64(irm.from_device_bf16(out)), lse.cpu().numpy().astype(np.float64)
+
+
+def test_decode_tiny():
+    """1 sequence, 16 heads, 1024 tokens in 8 chunks of 128 (chunk 0 fresh)."""
+    w = tiny_decode()
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    for S in (0, 1, 4, 16):
+        o, l = _gpu_decode(w, S)
+        assert rel_l2(o, o_ref) <= ATTN_TOL, S
+        assert np.max(np.abs(l - l_ref)) <= LSE_TOL, S
+
+
+@pytest.mark.parametrize("seed,heads,lens,splits", [
+    (1, 16, [1, 2, 31, 33, 64, 65], 0),
+    (2, 16, [700, 1500, 129], 3),
+    (3, 32, [2048, 100], 16),
+    (4, 128, [1000, 777], 4),
+    (5, 48, [3000], 7),
+    (6, 16, [5], 64),            # more splits than rows: empty splits
+])
+def test_decode_random(seed, heads, lens, splits):
+    w = random_table(seed, lens, heads=heads, p_hit=0.7, prefix_frac=0.3)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    o, l = _gpu_decode(w, splits)
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= LSE_TOL
+    for b in range(w.n_seq):          # every sequence, not only the aggregate
+        assert rel_l2(o[b], o_ref[b]) <= ATTN_TOL, b
+
+
+def test_decode_split_invariance_and_determinism():
+    w = random_table(11, [4096, 2500], heads=16)
+    o_ref, _ = _oracle_decode(w, range(w.n_seq))
+    res = {}
+    for S in (1, 4, 16):
+        res[S] = _gpu_decode(w, S)
+        assert rel_l2(res[S][0], o_ref) <= ATTN_TOL
+    again = _gpu_decode(w, 4)
+    assert np.array_equal(again[0], res[4][0]) and np.array_equal(again[1], res[4][1])
+
+
+def test_decode_fused_equals_gather_then_decode():
+    """Rotating on load equals assembling first and decoding the assembled
+    buffer as fresh rows (both round the rotated k_r to bf16 once)."""
+    w = random_table(12, [1500, 900, 64], heads=32)
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    fused = _gpu_decode(w, 4, table=t, pool=pool)
+    assembled = irm.rotate_gather(t, pool)
+    base = t.seq_base()
+    rows = [(int(base[s]), int(base[s + 1] - base[s]), 0, 0, FRESH) for s in range(t.n_seq)]
+    t2 = irm.Table(np.array(rows, CHUNK_DTYPE), np.arange(t.n_seq + 1, dtype=np.uint32),
+                   t.total_rows).upload()
+    plain = _gpu_decode(w, 4, table=t2, pool=assembled)
+    assert np.array_equal(fused[0], plain[0])
+    assert np.array_equal(fused[1], plain[1])
+
+
+def test_decode_batched_full_size_sampled():
+    """Batch 64 x 8192 tokens, 16 heads (benchmarked launch: default splits)."""
+    w = batched_decode()
+    o, l = _gpu_decode(w, w.n_splits)
+    seqs = [0, 17, 63]
+    o_ref, l_ref = _oracle_decode(w, seqs)
+    assert rel_l2(o[seqs], o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l[seqs] - l_ref)) <= LSE_TOL
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+def test_decode_long_full_size_sampled():
+    """Batch 32 x 32768 tokens, 128 heads, 16 splits (benchmarked launch)."""
+    w = long_decode()
+    o, l = _gpu_decode(w, w.n_splits)
+    seqs, heads = [0, 31], [0, 1, 63, 64, 127]
+    o_ref, l_ref = _oracle_decode(w, seqs, heads)
+    assert rel_l2(o[seqs][:, heads], o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l[seqs][:, heads] - l_ref)) <= LSE_TOL
+    assert np.all(np.isfinite(o))
+
+
+# ---------------------------------------------------------------- prefill
+def _oracle_prefill(w, qids):
+    inv = oracle.rope_inv_freq(w.theta)
+    (g, d, _), = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
+    c, k = oracle.assemble_rows(w.pool, g, d, inv)
+    return oracle.mla_prefill_tail(oracle.bf16_to_f64(w.q_lat), oracle.bf16_to_f64(w.q_rope), c, k,
+                                   w.q_pos0, w.scale, query_ids=qids)
+
+
+def _gpu_prefill(w):
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    out, lse = irm.mla_prefill_tail(ql, qr, w.q_pos0, t, pool, scale=w.scale, want_lse=True)
+    _sync()
+    return oracle.bf16_to_f64(irm.from_device_bf16(out)), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("seed,heads,N,nq", [
+    (21, 16, 700, 130), (22, 32, 333, 1), (23, 16, 64, 64), (24, 16, 95, 33), (25, 128, 520, 9),
+])
+def test_prefill_random(seed, heads, N, nq):
+    w = random_table(seed, [N], heads=heads, p_hit=0.7, prefix_frac=0.25, n_q=nq, kind="prefill")
+    o, l = _gpu_prefill(w)
+    o_ref, l_ref = _oracle_prefill(w, None)
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= LSE_TOL
+    for i in (0, nq - 1):
+        assert rel_l2(o[i], o_ref[i]) <= ATTN_TOL
+
+
+def test_prefill_last_query_equals_decode():
+    w = random_table(26, [1200], heads=16, n_q=7, kind="prefill")
+    o, l = _gpu_prefill(w)
+    from synth import Workload
+    wd = Workload("d", w.pool, w.chunks, w.seq_first, n_heads=16, q_lat=w.q_lat[-1:],
+                  q_rope=w.q_rope[-1:], kind="decode")
+    od, ld = _gpu_decode(wd, 1)
+    assert rel_l2(o[-1], od[0]) <= ATTN_TOL
+    assert np.max(np.abs(l[-1] - ld[0])) <= LSE_TOL
+
+
+def test_prefill_full_size_sampled():
+    """4096 queries at positions 61440.. over a 65536-row assembled cache."""
+    w = tail_prefill()
+    o, l = _gpu_prefill(w)
+    qids = [0, 1, 2047, 4094, 4095]
+    o_ref, l_ref = _oracle_prefill(w, qids)
+    assert rel_l2(o[qids], o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
+    assert np.all(np.isfinite(o))
+
+
+# ---------------------------------------------------------------- errors from the host
+def test_error_paths():
+    import torch
+    w = random_table(31, [200], heads=16, n_q=4, kind="prefill")
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    with pytest.raises(irm.IrmError) as e:
+        irm.mla_prefill_tail(ql, qr, 197, t, pool)
+    assert e.value.code == "ERANGE"
+    with pytest.raises(irm.IrmError) as e:
+        irm.mla_decode(ql[:1, :8].contiguous(), qr[:1, :8].contiguous(), t, pool)
+    assert e.value.code == "EUNSUPPORTED"
+    raw = irm.Table(w.chunks, w.seq_first, w.pool.shape[0])
+    with pytest.raises(irm.IrmError) as e:
+        irm.rotate_gather(raw, pool)
+    assert e.value.code == "EINVAL"
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    L = irm.lib()
+    out = torch.empty((1, 16, 512), dtype=torch.bfloat16, device="cuda")
+    st = L.irm_mla_decode(ql.data_ptr(), qr.data_ptr(), t.handle, pool.data_ptr(), pool.shape[0], 16, 2,
+                          0.07, out.data_ptr(), None, small.data_ptr(), 16, None)
+    assert irm.STATUS[st] == "EWORKSPACE"
+    with pytest.raises(irm.IrmError) as e:
+        irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(dev_buf=small)
+    assert e.value.code == "EWORKSPACE"
