@@ -234,44 +234,49 @@ __device__ __forceinline__ void tile_row_info(const Image& im, uint32_t g0, uint
   }
 }
 
-// Issue the global loads of one tile into registers (rows >= nrows read as 0).
+// One 64-row KV tile in registers.  Thread (wave w, lane l) holds c_KV unit l
+// of rows 4k + w (k = 0..15) and k_r unit tid % 8 of rows tid / 8 and
+// 32 + tid / 8: every load instruction of a wave reads 1 KB of one row.
+struct TileRegs {
+  uint4 c[16];
+  uint4 kr[2];
+};
+
+// Issue the global loads of one tile (rows >= nrows read as 0).
 __device__ __forceinline__ void load_tile(const uint4* __restrict__ pool, const uint32_t* s_src,
-                                          uint32_t nrows, uint4 (&v)[kUnitsPerThread]) {
-  const uint32_t nunits = nrows * kUnitsPerRow;
+                                          uint32_t nrows, TileRegs& v) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int k = 0; k < kUnitsPerThread; ++k) {
-    const uint32_t u = threadIdx.x + k * kThreads;
-    if (u < nunits) {
-      const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
-      v[k] = pool[(size_t)s_src[r] * kUnitsPerRow + c];
-    } else {
-      v[k] = make_uint4(0, 0, 0, 0);
-    }
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t r = 4 * k + w;
+    v.c[k] = (r < nrows) ? pool[(size_t)s_src[r] * kUnitsPerRow + l] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t r = (threadIdx.x >> 3) + 32 * j;
+    v.kr[j] = (r < nrows) ? pool[(size_t)s_src[r] * kUnitsPerRow + kLatUnits + (threadIdx.x & 7)]
+                          : make_uint4(0, 0, 0, 0);
   }
 }
 
 // Rotate the k_r units held in registers (reads s_rot of the same tile).
-__device__ __forceinline__ void rotate_tile_regs(const float2* __restrict__ trig,
-                                                 const uint32_t* s_rot,
-                                                 uint4 (&v)[kUnitsPerThread]) {
+__device__ __forceinline__ void rotate_tile_regs(const float2* __restrict__ trig, const uint32_t* s_rot,
+                                                 TileRegs& v) {
 #pragma unroll
-  for (int k = 0; k < kUnitsPerThread; ++k) {
-    const uint32_t u = threadIdx.x + k * kThreads;
-    const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
-    if (c >= (uint32_t)kLatUnits) {
-      const uint32_t e = s_rot[r];
-      if (e != kNoRot) v[k] = rotate_unit(v[k], trig + (size_t)e * irm::kPairs + (c - kLatUnits) * 4);
-    }
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t e = s_rot[(threadIdx.x >> 3) + 32 * j];
+    if (e != kNoRot) v.kr[j] = rotate_unit(v.kr[j], trig + (size_t)e * irm::kPairs + (threadIdx.x & 7) * 4);
   }
 }
 
-__device__ __forceinline__ void store_tile_lds(unsigned char* lds, const uint4 (&v)[kUnitsPerThread]) {
+__device__ __forceinline__ void store_tile_lds(unsigned char* lds, const TileRegs& v) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int k = 0; k < kUnitsPerThread; ++k) {
-    const uint32_t u = threadIdx.x + k * kThreads;
-    const uint32_t r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
-    *reinterpret_cast<uint4*>(lds + r * kLdsRow + c * 16) = v[k];
-  }
+  for (int k = 0; k < 16; ++k) *reinterpret_cast<uint4*>(lds + (4 * k + w) * kLdsRow + 16 * l) = v.c[k];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    *reinterpret_cast<uint4*>(lds + ((threadIdx.x >> 3) + 32 * j) * kLdsRow + 2 * IRM_D_LATENT +
+                              16 * (threadIdx.x & 7)) = v.kr[j];
 }
 
 // S^T for tile rows [row0, row0+16): lane (q = lane/16, r = lane%16) gets the
@@ -360,8 +365,83 @@ __device__ __forceinline__ void load_q(const uint4* __restrict__ q_lat, const ui
   for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = __builtin_bit_cast(bf16x8_t, pr[4 * kk]);
 }
 
+// PV over a pair of 16-row blocks on v_mfma_f32_16x16x32_bf16:
+// O^T[n][head] += C^T[n][k] P^T[k][head], k = 32 tile rows.  The A operand
+// (8 consecutive k per lane) comes from two transposing LDS reads
+// (ds_read_b64_tr_b16): within each 16-lane group, lane 4a+b receives element
+// b of the 8-byte reads of lanes a, a+4, a+8, a+12.  Lane (q, s) therefore
+// reads row row0 + 4q + s/4, columns n0 + 4(s%4)..+3, and gets C[row0 + 4q + i]
+// [n0 + s] for i = 0..3; the second read covers rows row0 + 16 + 4q + i.  The
+// k order {4q..4q+3, 16+4q..16+4q+3} matches the lane's P^T values of the two
+// score blocks, so pb is just those 8 probabilities.
+typedef short i16x4_lds_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t tr_pair(const unsigned char* p0, const unsigned char* p1) {
+  typedef __attribute__((address_space(3))) i16x4_lds_t* lds_ptr_t;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(p0));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(p1));
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int NB>
+__device__ __forceinline__ void pv_pair(const unsigned char* lds, int row0, int nb0, bf16x8_t pb,
+                                        f32x4_t (&o)[NB]) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, s = lane & 15;
+  const unsigned char* p0 = lds + (row0 + 4 * q + (s >> 2)) * kLdsRow + 8 * (s & 3) + 32 * nb0;
+  const unsigned char* p1 = p0 + 16 * kLdsRow;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const bf16x8_t a = tr_pair(p0 + 32 * nb, p1 + 32 * nb);
+    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[nb], 0, 0, 0);
+  }
+}
+
+template <int NB, int NO>
+__device__ __forceinline__ void softmax_update_n(float (&s)[NB][4], float& m, float& l,
+                                                 f32x4_t (&o)[NO], float (&p)[NB][4]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = exp2f(m - m_use);  // m == -inf gives 0
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[j][i] = exp2f(s[j][i] - m_use);
+      sum += p[j][i];
+    }
+  l = l * alpha + sum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int nb = 0; nb < NO; ++nb) o[nb] *= alpha;
+  }
+  m = m_new;
+}
+
+__device__ __forceinline__ bf16x8_t pack_p8(const float (&a)[4], const float (&b)[4]) {
+  const uint4 w = make_uint4(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]),
+                             pack_bf16(b[2], b[3]));
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
 // ---------------------------------------------------------------------------
 // split-KV decode, pass 1
+//
+// Workgroup = (sequence, split, block of HG head groups of 16), 4 waves.
+// Wave w serves head group w / CG and output columns [512/CG * (w % CG), ..):
+// every wave scores all 64 rows of a tile for its 16 heads (the CG waves of a
+// head group repeat the same score work and reach bit-identical softmax
+// state), then accumulates only its column slice, so each lane holds 128/CG
+// accumulators and no cross-wave merge is needed.
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
   Image im;
@@ -370,21 +450,23 @@ struct DecodeArgs {
   const uint4* q_rope;
   float* ws_acc;  // [n_seq][n_splits][n_heads][512], unnormalised
   float* ws_ml;   // [n_seq][n_splits][n_heads][2]: base-2 max, sum
-  uint32_t n_seq, n_heads, n_groups, n_splits;
+  uint32_t n_seq, n_heads, n_gblocks, n_splits;
   float scale_log2;
 };
 
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+template <int HG, int CG>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a) {
+  static_assert(HG * CG == kThreads / 64, "one wave per (head group, column group)");
+  constexpr int kNB = 32 / CG;  // 16-column output blocks per wave
   __shared__ __attribute__((aligned(16))) unsigned char s_tile[kTile * kLdsRow];
   __shared__ uint32_t s_src[kTile];
   __shared__ uint32_t s_rot[kTile];
-  __shared__ float s_ml[4][16][2];
 
-  // Workgroups of the same (sequence, split) but different head groups get
-  // the same x % 8, i.e. the same XCD and L2, and consecutive slots there.
+  // Workgroups of the same (sequence, split) but different head-group blocks
+  // get the same x % 8, i.e. the same XCD and L2, at consecutive slots.
   const uint32_t x = blockIdx.x, xcd = x & 7, slot = x >> 3;
-  const uint32_t g = slot % a.n_groups;
-  const uint32_t bs = (slot / a.n_groups) * 8 + xcd;
+  const uint32_t gb = slot % a.n_gblocks;
+  const uint32_t bs = (slot / a.n_gblocks) * 8 + xcd;
   if (bs >= a.n_seq * a.n_splits) return;
   const uint32_t b = bs / a.n_splits, sp = bs % a.n_splits;
 
@@ -395,18 +477,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hq = lane >> 4, hr = lane & 15;
-  const uint32_t head = g * 16 + hr;
+  const int hg = wave / CG, cg = wave % CG;
+  const uint32_t head = (gb * HG + hg) * 16 + hr;
 
   bf16x8_t qb[18];
   load_q(a.q_lat, a.q_rope, b, a.n_heads, head, qb);
 
-  f32x4_t o[32];
+  f32x4_t o[kNB];
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
   const uint32_t ntiles = (r1 - r0 + kTile - 1) / kTile;
-  uint4 v[kUnitsPerThread];
+  TileRegs v;
   if (ntiles > 0) {
     tile_row_info(a.im, base + r0, min((uint32_t)kTile, r1 - r0), s_src, s_rot);
     __syncthreads();
@@ -416,71 +499,41 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const uint32_t t0 = r0 + t * kTile;
     const uint32_t nrows = min((uint32_t)kTile, r1 - t0);
     rotate_tile_regs(a.im.trig, s_rot, v);
-    __syncthreads();  // previous tile fully consumed, row info of this tile no longer needed
+    __syncthreads();  // previous tile consumed; row info of this tile no longer needed
     store_tile_lds(s_tile, v);
-    if (t + 1 < ntiles) {
-      const uint32_t n1 = min((uint32_t)kTile, r1 - (t0 + kTile));
-      tile_row_info(a.im, base + t0 + kTile, n1, s_src, s_rot);
-    }
+    if (t + 1 < ntiles) tile_row_info(a.im, base + t0 + kTile, min((uint32_t)kTile, r1 - t0 - kTile), s_src, s_rot);
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(a.pool, s_src, min((uint32_t)kTile, r1 - (t0 + kTile)), v);
+    if (t + 1 < ntiles) load_tile(a.pool, s_src, min((uint32_t)kTile, r1 - t0 - kTile), v);
 
-    // this wave: tile rows [16 wave, 16 wave + 16)
-    const int row0 = 16 * wave;
-    if ((uint32_t)row0 < nrows) {
-      const f32x4_t acc = qk_block(s_tile, row0, qb);
-      float s[1][4];
+    float sc[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s[0][i] = ((uint32_t)(row0 + 4 * hq + i) < nrows) ? acc[i] * a.scale_log2 : -INFINITY;
-      i16x4_t pb[1];
-      softmax_update<1>(s, m, l, o, pb);
-      pv_block(s_tile, row0, pb[0], o);
-    }
-  }
-
-  // merge the 4 waves: sum l over the 4 lanes of each head, then combine
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (hq == 0) {
-    s_ml[wave][hr][0] = m;
-    s_ml[wave][hr][1] = l;
-  }
-  __syncthreads();
-  float mstar = -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      if ((uint32_t)(16 * j) < nrows) {
+        const f32x4_t acc = qk_block(s_tile, 16 * j, qb);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) mstar = fmaxf(mstar, s_ml[w][hr][0]);
-  float lsum = 0.f;
+        for (int i = 0; i < 4; ++i)
+          sc[j][i] = ((uint32_t)(16 * j + 4 * hq + i) < nrows) ? acc[i] * a.scale_log2 : -INFINITY;
+      } else {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = s_ml[w][hr][0];
-    if (mw != -INFINITY) lsum += s_ml[w][hr][1] * exp2f(mw - mstar);
-  }
-  const float f = (m == -INFINITY) ? 0.f : exp2f(m - mstar);
-  float* red = reinterpret_cast<float*>(s_tile);  // [16 heads][512]
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int nb = 0; nb < 32; ++nb) {
-        float4* dst = reinterpret_cast<float4*>(red + hr * IRM_D_LATENT + 16 * nb + 4 * hq);
-        float4 cur = (w == 0) ? make_float4(0.f, 0.f, 0.f, 0.f) : *dst;
-        cur.x += f * o[nb][0];
-        cur.y += f * o[nb][1];
-        cur.z += f * o[nb][2];
-        cur.w += f * o[nb][3];
-        *dst = cur;
+        for (int i = 0; i < 4; ++i) sc[j][i] = -INFINITY;
       }
     }
-    __syncthreads();
+    float p[4][4];
+    softmax_update_n<4, kNB>(sc, m, l, o, p);
+    pv_pair<kNB>(s_tile, 0, cg * kNB, pack_p8(p[0], p[1]), o);
+    if (nrows > 32) pv_pair<kNB>(s_tile, 32, cg * kNB, pack_p8(p[2], p[3]), o);
   }
-  // write the partial of this (sequence, split, head group)
-  const size_t pidx = ((size_t)b * a.n_splits + sp) * a.n_heads + g * 16;
-  const float4* src = reinterpret_cast<const float4*>(red);
-  float4* dst = reinterpret_cast<float4*>(a.ws_acc + pidx * IRM_D_LATENT);
-  for (int i = threadIdx.x; i < 16 * IRM_D_LATENT / 4; i += kThreads) dst[i] = src[i];
-  if (threadIdx.x < 16) {
-    a.ws_ml[(pidx + threadIdx.x) * 2 + 0] = mstar;
-    a.ws_ml[(pidx + threadIdx.x) * 2 + 1] = (mstar == -INFINITY) ? 0.f : lsum;
+
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const size_t pidx = ((size_t)b * a.n_splits + sp) * a.n_heads + head;
+  float* dst = a.ws_acc + pidx * IRM_D_LATENT + 16 * cg * kNB + 4 * hq;
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+    *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[nb][0], o[nb][1], o[nb][2], o[nb][3]);
+  if (cg == 0 && hq == 0) {
+    a.ws_ml[pidx * 2 + 0] = m;
+    a.ws_ml[pidx * 2 + 1] = (m == -INFINITY) ? 0.f : l;
   }
 }
 
@@ -559,7 +612,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY, l = 0.f;
 
   const uint32_t ntiles = (rows + kTile - 1) / kTile;
-  uint4 v[kUnitsPerThread];
+  TileRegs v;
   tile_row_info(a.im, base, min((uint32_t)kTile, rows), s_src, s_rot);
   __syncthreads();
   load_tile(a.pool, s_src, min((uint32_t)kTile, rows), v);
@@ -648,6 +701,9 @@ irm_status check_pool(const irm_table* t, const void* pool, uint64_t pool_rows, 
     return fail(IRM_ERANGE, std::string(fn) + ": pool has fewer rows than the table was built for");
   return IRM_OK;
 }
+
+// Head groups of 16 handled by one decode workgroup for G = n_heads / 16.
+uint32_t heads_per_block(uint32_t G) { return (G % 2 == 0 && G < 4) ? 2 : 1; }
 
 uint32_t default_splits(const irm_table* t, uint32_t n_groups) {
   // aim for >= 2 workgroups per CU (256 CUs) with >= 256 rows per split
@@ -740,7 +796,7 @@ extern "C" irm_status irm_mla_decode_workspace(const irm_table* t, uint32_t n_he
   if (!t || !bytes) return fail(IRM_EINVAL, "irm_mla_decode_workspace: NULL argument");
   irm_status st = check_heads(n_heads, "irm_mla_decode_workspace");
   if (st != IRM_OK) return st;
-  const uint32_t S = n_splits ? n_splits : default_splits(t, n_heads / 16);
+  const uint32_t S = n_splits ? n_splits : default_splits(t, (n_heads / 16) / heads_per_block(n_heads / 16));
   const size_t parts = (size_t)t->n_seq * S * n_heads;
   *bytes = irm::align_up(parts * IRM_D_LATENT * sizeof(float)) + irm::align_up(parts * 2 * sizeof(float));
   return IRM_OK;
@@ -761,7 +817,7 @@ extern "C" irm_status irm_mla_decode(const void* q_latent, const void* q_rope, c
     return fail(IRM_EINVAL, "irm_mla_decode: q_latent, q_rope and out must be non-NULL and 16-byte aligned");
   if (n_splits > 4096) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: n_splits above 4096");
   const uint32_t G = n_heads / 16;
-  const uint32_t S = n_splits ? n_splits : default_splits(t, G);
+  const uint32_t S = n_splits ? n_splits : default_splits(t, G / heads_per_block(G));
   size_t need = 0;
   irm_mla_decode_workspace(t, n_heads, S, &need);
   if (!workspace || ws_bytes < need || reinterpret_cast<uintptr_t>(workspace) % irm::kAlign)
@@ -779,14 +835,21 @@ extern "C" irm_status irm_mla_decode(const void* q_latent, const void* q_rope, c
                                      irm::align_up(parts * IRM_D_LATENT * sizeof(float)));
   a.n_seq = t->n_seq;
   a.n_heads = n_heads;
-  a.n_groups = G;
   a.n_splits = S;
   a.scale_log2 = scale * kLog2e;
+  // head groups per workgroup: 1 (4 column slices), 2 (2 slices) or 4 (full rows)
+  const int hg = (int)heads_per_block(G);
+  a.n_gblocks = G / hg;
   const uint64_t bs = (uint64_t)t->n_seq * S;
-  const uint64_t grid = (bs + 7) / 8 * 8 * G;
+  const uint64_t grid = (bs + 7) / 8 * 8 * a.n_gblocks;
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(decode_split_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+  if (hg == 4)
+    hipLaunchKernelGGL((decode_split_kernel<4, 1>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+  else if (hg == 2)
+    hipLaunchKernelGGL((decode_split_kernel<2, 2>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<1, 4>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   if ((st = launch_check("irm_mla_decode: split kernel")) != IRM_OK) return st;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(t->n_seq * n_heads), dim3(128), 0, s, a.ws_acc, a.ws_ml,
                      static_cast<uint16_t*>(out), lse, n_heads, S);
