@@ -205,7 +205,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="gather,decode,long_decode,prefill")
+    ap.add_argument("--legs", default="gather,decode,long_decode,prefill",
+                    help="comma list; without gather only the named legs run (profiling, no JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -236,6 +237,16 @@ def main():
         return
 
     legs = [x.strip() for x in args.legs.split(",") if x.strip()]
+    if "gather" not in legs:
+        # profiling mode: run the requested legs only, no JSON line
+        for name in legs:
+            if name == "decode":
+                leg_decode(args, irm, torch, synth, "batched decode", synth.batched_decode)
+            elif name == "long_decode":
+                leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)
+            elif name == "prefill":
+                leg_prefill(args, irm, torch, synth)
+        return
     g = leg_gather(args, irm, torch, synth)
     extra = {}
     if "decode" in legs:

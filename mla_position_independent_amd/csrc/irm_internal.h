@@ -32,11 +32,13 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
-// Device image: [entries | seq_first | seq_base | block_map | trig].
-// trig (float2 cos/sin per entry and pair) is last and is computed on the GPU.
+// Device image: [entries | seq_first | seq_base | block_map | trig | rowmap].
+// The host copies everything before trig; trig (float2 cos/sin per entry and
+// pair) and the row map (uint2 {pool row, entry or ~0u if not rotated} per
+// assembled row) are computed on the GPU.
 struct ImageLayout {
   size_t off_entries = 0, off_seq_first = 0, off_seq_base = 0, off_block_map = 0;
-  size_t off_trig = 0, bytes = 0;
+  size_t off_trig = 0, off_rowmap = 0, bytes = 0;
 };
 
 }  // namespace irm

@@ -54,6 +54,8 @@ struct Image {
   const uint32_t* seq_base;
   const uint32_t* block_map;
   const float2* trig;
+  const uint2* rowmap;
+  uint32_t n_entries;
 };
 
 Image image_of(const irm_table* t) {
@@ -64,6 +66,8 @@ Image image_of(const irm_table* t) {
   im.seq_base = reinterpret_cast<const uint32_t*>(d + t->layout.off_seq_base);
   im.block_map = reinterpret_cast<const uint32_t*>(d + t->layout.off_block_map);
   im.trig = reinterpret_cast<const float2*>(d + t->layout.off_trig);
+  im.rowmap = reinterpret_cast<const uint2*>(d + t->layout.off_rowmap);
+  im.n_entries = t->n_chunks;
   return im;
 }
 
@@ -138,6 +142,17 @@ __global__ void gather_index_kernel(Image im, uint32_t total_rows, int64_t* __re
 }
 
 // ---------------------------------------------------------------------------
+// row map: {pool row, entry if rotated else kNoRot} per assembled row
+// ---------------------------------------------------------------------------
+__global__ void rowmap_kernel(Image im, uint32_t total_rows, uint2* __restrict__ rowmap) {
+  const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= total_rows) return;
+  const uint32_t e = find_entry(im, g);
+  const DevEntry d = im.ents[e];
+  rowmap[g] = make_uint2(d.pool_row + (g - d.out_row), d.delta != 0 ? e : kNoRot);
+}
+
+// ---------------------------------------------------------------------------
 // rotate-gather: one workgroup per 64 assembled rows, flat 16-byte units
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void rotate_gather_kernel(Image im, uint32_t total_rows,
@@ -207,148 +222,177 @@ __global__ __launch_bounds__(kThreads) void rotate_gather_kernel(Image im, uint3
 // attention building blocks (shared by decode and tail-prefill)
 //
 // A workgroup of 4 waves streams KV tiles of 64 rows through LDS (padded
-// row-major, c_KV and rotated k_r).  The score block of 16 rows x 16 heads
-// is S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T from
-// registers), so each lane ends with 4 rows of one head; P^T in that layout
-// is directly the B operand of v_mfma_f32_16x16x16_bf16 for O^T = C^T P^T,
-// whose C^T operand is read column-wise from LDS.  O^T leaves every lane with
-// 128 outputs of a single head, so the online-softmax rescale is lane-local.
+// row-major, c_KV and rotated k_r).  Tile t+1 is loaded into registers while
+// tile t is computed; the row map of tile t+2 is already in LDS and that of
+// tile t+3 is in flight, so no dependent table lookup sits on the critical
+// path.  k_r is rotated in registers between the global load and the LDS
+// store, with the entry's (cos, sin) fetched together with the data.
+//
+// The score block of 16 rows x 16 heads is S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16 (K from LDS, Q^T from registers), so each lane
+// ends with 4 rows of one head; O^T = C^T P^T then leaves every lane with
+// outputs of a single head, so the online-softmax rescale is lane-local.
 // Softmax runs in the base-2 domain (scores pre-multiplied by scale*log2 e).
 // ---------------------------------------------------------------------------
 
-// Row info of a tile: pool row and rotation entry (or kNoRot) per tile row.
-__device__ __forceinline__ void tile_row_info(const Image& im, uint32_t g0, uint32_t nrows,
-                                              uint32_t* s_src, uint32_t* s_rot) {
-  const int t = threadIdx.x;
-  if (t < kTile) {
-    uint32_t src = 0, rot = kNoRot;
-    if ((uint32_t)t < nrows) {
-      const uint32_t g = g0 + t;
-      const uint32_t e = find_entry(im, g);
-      const DevEntry d = im.ents[e];
-      src = d.pool_row + (g - d.out_row);
-      rot = d.delta != 0 ? e : kNoRot;
-    }
-    s_src[t] = src;
-    s_rot[t] = rot;
+// One 64-row KV tile in registers.  Thread (wave w, lane l) holds c_KV unit l
+// of rows 16w + k (k = 0..15) and k_r unit tid % 8 of rows tid / 8 and
+// 32 + tid / 8 (every c_KV load instruction of a wave reads 1 KB of one row),
+// plus the (cos, sin) of the 4 pairs of each k_r unit.
+struct TileRegs {
+  u32x4_t c[16];
+  u32x4_t kr[2];
+  f32x4_t tr[2][2];
+  uint32_t rot;  // bit j: k_r unit j is rotated
+};
+
+// Row-map record of tile row tid (threads 0..63): {pool row, entry or kNoRot}.
+// Rows past the end map to pool row 0 (any valid row: their scores are
+// masked, and finite data keeps 0 * value = 0 in the PV product).
+__device__ __forceinline__ uint2 load_rowmap(const uint2* __restrict__ rowmap, uint32_t g0,
+                                             uint32_t nrows) {
+  const uint32_t t = threadIdx.x;
+  return (t < nrows) ? rowmap[g0 + t] : make_uint2(0u, kNoRot);
+}
+
+__device__ __forceinline__ void put_rowmap(uint2 rec, uint32_t* s_src, uint32_t* s_rot) {
+  if (threadIdx.x < kTile) {
+    s_src[threadIdx.x] = rec.x;
+    s_rot[threadIdx.x] = rec.y;
   }
 }
 
-// One 64-row KV tile in registers.  Thread (wave w, lane l) holds c_KV unit l
-// of rows 4k + w (k = 0..15) and k_r unit tid % 8 of rows tid / 8 and
-// 32 + tid / 8: every load instruction of a wave reads 1 KB of one row.
-struct TileRegs {
-  uint4 c[16];
-  uint4 kr[2];
-};
-
-// Issue the global loads of one tile (rows >= nrows read as 0).
-__device__ __forceinline__ void load_tile(const uint4* __restrict__ pool, const uint32_t* s_src,
-                                          uint32_t nrows, TileRegs& v) {
+// Issue the global loads of one tile, branch free so that all of them are in
+// flight together.  Pool rows and entries come from the validated row map;
+// they are also clamped so that a corrupted map shows up as a wrong result,
+// never as a fault.
+__device__ __forceinline__ void issue_tile(const uint4* __restrict__ pool, uint32_t pool_last,
+                                           const float2* __restrict__ trig, uint32_t ent_last,
+                                           const uint32_t* s_src, const uint32_t* s_rot, TileRegs& v) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const u32x4_t* P = reinterpret_cast<const u32x4_t*>(pool);
+  const u32x4_t* rows = reinterpret_cast<const u32x4_t*>(s_src + 16 * w);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const uint32_t r = 4 * k + w;
-    v.c[k] = (r < nrows) ? pool[(size_t)s_src[r] * kUnitsPerRow + l] : make_uint4(0, 0, 0, 0);
+  for (int q = 0; q < 4; ++q) {
+    const u32x4_t x = rows[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v.c[4 * q + i] = P[(size_t)min(x[i], pool_last) * kUnitsPerRow + l];
   }
+  v.rot = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint32_t r = (threadIdx.x >> 3) + 32 * j;
-    v.kr[j] = (r < nrows) ? pool[(size_t)s_src[r] * kUnitsPerRow + kLatUnits + (threadIdx.x & 7)]
-                          : make_uint4(0, 0, 0, 0);
+    const uint32_t e = s_rot[r];
+    v.kr[j] = P[(size_t)min(s_src[r], pool_last) * kUnitsPerRow + kLatUnits + (threadIdx.x & 7)];
+    const f32x4_t* tp = reinterpret_cast<const f32x4_t*>(trig + (size_t)min(e, ent_last) * irm::kPairs +
+                                                         (threadIdx.x & 7) * 4);
+    v.tr[j][0] = tp[0];
+    v.tr[j][1] = tp[1];
+    v.rot |= (e != kNoRot ? 1u : 0u) << j;
   }
 }
 
-// Rotate the k_r units held in registers (reads s_rot of the same tile).
-__device__ __forceinline__ void rotate_tile_regs(const float2* __restrict__ trig, const uint32_t* s_rot,
-                                                 TileRegs& v) {
+// One rotation pair: (x, y) packed as bf16 in w, (cos, sin) = (c, s).
+__device__ __forceinline__ uint32_t rotate_pair(uint32_t w, float c, float s) {
+  const float x = bf16_lo(w), y = bf16_hi(w);
+  return pack_bf16(fmaf(x, c, -(y * s)), fmaf(x, s, y * c));
+}
+
+__device__ __forceinline__ void rotate_tile(TileRegs& v) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const uint32_t e = s_rot[(threadIdx.x >> 3) + 32 * j];
-    if (e != kNoRot) v.kr[j] = rotate_unit(v.kr[j], trig + (size_t)e * irm::kPairs + (threadIdx.x & 7) * 4);
+    const f32x4_t a = v.tr[j][0], b = v.tr[j][1];
+    const u32x4_t k = v.kr[j];
+    const u32x4_t r = {rotate_pair(k[0], a[0], a[1]), rotate_pair(k[1], a[2], a[3]),
+                       rotate_pair(k[2], b[0], b[1]), rotate_pair(k[3], b[2], b[3])};
+    v.kr[j] = ((v.rot >> j) & 1u) ? r : k;
   }
 }
 
 __device__ __forceinline__ void store_tile_lds(unsigned char* lds, const TileRegs& v) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) *reinterpret_cast<uint4*>(lds + (4 * k + w) * kLdsRow + 16 * l) = v.c[k];
+  for (int k = 0; k < 16; ++k) *reinterpret_cast<u32x4_t*>(lds + (16 * w + k) * kLdsRow + 16 * l) = v.c[k];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    *reinterpret_cast<uint4*>(lds + ((threadIdx.x >> 3) + 32 * j) * kLdsRow + 2 * IRM_D_LATENT +
-                              16 * (threadIdx.x & 7)) = v.kr[j];
+    *reinterpret_cast<u32x4_t*>(lds + ((threadIdx.x >> 3) + 32 * j) * kLdsRow + 2 * IRM_D_LATENT +
+                                16 * (threadIdx.x & 7)) = v.kr[j];
 }
 
-// S^T for tile rows [row0, row0+16): lane (q = lane/16, r = lane%16) gets the
-// scores of rows row0 + 4q + i (i = 0..3) for head r.
-__device__ __forceinline__ f32x4_t qk_block(const unsigned char* lds, int row0,
-                                            const bf16x8_t (&qb)[18]) {
+// Shared memory of the tile pipeline.
+struct TileSmem {
+  unsigned char tile[kTile * kLdsRow];
+  uint32_t src[3][kTile];
+  uint32_t rot[3][kTile];
+};
+
+// Stream the assembled rows [g_begin, g_begin + n) through LDS in 64-row
+// tiles, calling compute(t, nrows) with tile t resident in sm.tile.  With
+// kDepth = 2 the loads of tiles t+1 and t+2 are in flight while tile t is
+// computed (two register sets); with kDepth = 1 only tile t+1 is.  The row
+// map runs kDepth + 1 tiles ahead in LDS and one more in registers.  Every
+// thread of the workgroup must call this with the same arguments.
+template <int kDepth, class Compute>
+__device__ __forceinline__ void stream_tiles(const Image& im, const uint2* __restrict__ rowmap,
+                                             const uint4* __restrict__ pool, uint32_t pool_last,
+                                             uint32_t g_begin, uint32_t n, TileSmem& sm, Compute&& compute) {
+  static_assert(kDepth == 1 || kDepth == 2, "pipeline depth 1 or 2");
+  const uint32_t ntiles = (n + kTile - 1) / kTile;
+  if (ntiles == 0) return;
+  auto rows_of = [&](uint32_t t) { return min((uint32_t)kTile, n - t * kTile); };
+  for (uint32_t t = 0; t <= (uint32_t)kDepth && t < ntiles; ++t)
+    put_rowmap(load_rowmap(rowmap, g_begin + t * kTile, rows_of(t)), sm.src[t % 3], sm.rot[t % 3]);
+  __syncthreads();
+  TileRegs va, vb;
+  issue_tile(pool, pool_last, im.trig, im.n_entries - 1, sm.src[0], sm.rot[0], va);
+  if (kDepth == 2 && ntiles > 1) issue_tile(pool, pool_last, im.trig, im.n_entries - 1, sm.src[1], sm.rot[1], vb);
+  uint2 ri = make_uint2(0u, kNoRot);
+  if (ntiles > kDepth + 1) ri = load_rowmap(rowmap, g_begin + (kDepth + 1) * kTile, rows_of(kDepth + 1));
+
+  // one pipeline step on register set v (which holds tile t)
+#define IRM_PIPE_STEP(t, v)                                                                          \
+  do {                                                                                               \
+    rotate_tile(v);                                                                                  \
+    __syncthreads(); /* every wave is done with tile t-1 */                                          \
+    store_tile_lds(sm.tile, v);                                                                      \
+    /* the row map of tile x always lives in slot x % 3 */                                           \
+    if ((t) + kDepth + 1 < ntiles)                                                                   \
+      put_rowmap(ri, sm.src[((t) + kDepth + 1) % 3], sm.rot[((t) + kDepth + 1) % 3]);                \
+    __syncthreads(); /* tile t and the row map of tile t+kDepth+1 are visible */                     \
+    const uint32_t tn = (t) + kDepth;                                                                \
+    if (tn < ntiles) issue_tile(pool, pool_last, im.trig, im.n_entries - 1, sm.src[tn % 3], sm.rot[tn % 3], v); \
+    if (tn + 2 < ntiles) ri = load_rowmap(rowmap, g_begin + (tn + 2) * kTile, rows_of(tn + 2));     \
+    compute((t), rows_of(t));                                                                        \
+  } while (0)
+  if constexpr (kDepth == 1) {
+    for (uint32_t t = 0; t < ntiles; ++t) IRM_PIPE_STEP(t, va);
+  } else {
+    for (uint32_t t = 0; t < ntiles; t += 2) {
+      IRM_PIPE_STEP(t, va);
+      if (t + 1 < ntiles) IRM_PIPE_STEP(t + 1, vb);
+    }
+  }
+#undef IRM_PIPE_STEP
+}
+
+// S^T for the four 16-row blocks of a tile: lane (q = lane/16, r = lane%16)
+// gets in acc[j] the scores of rows 16j + 4q + i (i = 0..3) for head r.  The
+// four blocks are interleaved so that LDS reads overlap independent MFMAs.
+__device__ __forceinline__ void qk_tile(const unsigned char* lds, const bf16x8_t (&qb)[18],
+                                        f32x4_t (&acc)[4]) {
   const int lane = threadIdx.x & 63;
-  const unsigned char* p = lds + (row0 + (lane & 15)) * kLdsRow + (lane >> 4) * 16;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const unsigned char* p = lds + (lane & 15) * kLdsRow + (lane >> 4) * 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 18; ++kk) {
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + kk * 64));
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kk], acc, 0, 0, 0);
+    bf16x8_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + 16 * j * kLdsRow + kk * 64));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], qb[kk], acc[j], 0, 0, 0);
   }
-  return acc;
-}
-
-// O^T[n][head] += C^T[n][rows row0+4q..+3] P^T[rows][head] for all 512 n.
-__device__ __forceinline__ void pv_block(const unsigned char* lds, int row0, i16x4_t pb,
-                                         f32x4_t (&o)[32]) {
-  const int lane = threadIdx.x & 63;
-  const unsigned short* base =
-      reinterpret_cast<const unsigned short*>(lds + (row0 + 4 * (lane >> 4)) * kLdsRow) + (lane & 15);
-  constexpr int kStride = kLdsRow / 2;
-#pragma unroll
-  for (int nb = 0; nb < 32; ++nb) {
-    i16x4_t a;
-    a.x = (short)base[16 * nb];
-    a.y = (short)base[kStride + 16 * nb];
-    a.z = (short)base[2 * kStride + 16 * nb];
-    a.w = (short)base[3 * kStride + 16 * nb];
-    o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o[nb], 0, 0, 0);
-  }
-}
-
-// Online softmax for one head per lane over `nb` blocks of 4 scores each.
-// s[] holds base-2 scaled scores (-inf where masked).  Updates m and the
-// lane-local partial l, rescales o when the max moved, and returns P^T
-// (bf16) per block in pb[].
-template <int NB>
-__device__ __forceinline__ void softmax_update(float (&s)[NB][4], float& m, float& l,
-                                               f32x4_t (&o)[32], i16x4_t (&pb)[NB]) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = exp2f(m - m_use);  // m == -inf gives 0
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = exp2f(s[j][i] - m_use);
-      sum += p[i];
-    }
-    pb[j].x = (short)bf16_rne(p[0]);
-    pb[j].y = (short)bf16_rne(p[1]);
-    pb[j].z = (short)bf16_rne(p[2]);
-    pb[j].w = (short)bf16_rne(p[3]);
-  }
-  l = l * alpha + sum;
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int nb = 0; nb < 32; ++nb) o[nb] *= alpha;
-  }
-  m = m_new;
 }
 
 // Q^T operands of one head group for one query: lane (q, r) holds head
@@ -443,6 +487,10 @@ __device__ __forceinline__ bf16x8_t pack_p8(const float (&a)[4], const float (&b
 // state), then accumulates only its column slice, so each lane holds 128/CG
 // accumulators and no cross-wave merge is needed.
 // ---------------------------------------------------------------------------
+// Tile pipeline depth of the decode kernel: 1 = one tile in flight with two
+// workgroups per CU, 2 = two tiles in flight with one workgroup per CU.
+constexpr int kDecodeDepth = 1;
+
 struct DecodeArgs {
   Image im;
   const uint4* pool;
@@ -451,16 +499,15 @@ struct DecodeArgs {
   float* ws_acc;  // [n_seq][n_splits][n_heads][512], unnormalised
   float* ws_ml;   // [n_seq][n_splits][n_heads][2]: base-2 max, sum
   uint32_t n_seq, n_heads, n_gblocks, n_splits;
+  uint32_t pool_last;  // last valid pool row
   float scale_log2;
 };
 
-template <int HG, int CG>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a) {
+template <int HG, int CG, int kDepth>
+__global__ __launch_bounds__(kThreads, 3 - kDepth) void decode_split_kernel(DecodeArgs a) {
   static_assert(HG * CG == kThreads / 64, "one wave per (head group, column group)");
   constexpr int kNB = 32 / CG;  // 16-column output blocks per wave
-  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kTile * kLdsRow];
-  __shared__ uint32_t s_src[kTile];
-  __shared__ uint32_t s_rot[kTile];
+  __shared__ __attribute__((aligned(16))) TileSmem sm;
 
   // Workgroups of the same (sequence, split) but different head-group blocks
   // get the same x % 8, i.e. the same XCD and L2, at consecutive slots.
@@ -488,41 +535,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  const uint32_t ntiles = (r1 - r0 + kTile - 1) / kTile;
-  TileRegs v;
-  if (ntiles > 0) {
-    tile_row_info(a.im, base + r0, min((uint32_t)kTile, r1 - r0), s_src, s_rot);
-    __syncthreads();
-    load_tile(a.pool, s_src, min((uint32_t)kTile, r1 - r0), v);
-  }
-  for (uint32_t t = 0; t < ntiles; ++t) {
-    const uint32_t t0 = r0 + t * kTile;
-    const uint32_t nrows = min((uint32_t)kTile, r1 - t0);
-    rotate_tile_regs(a.im.trig, s_rot, v);
-    __syncthreads();  // previous tile consumed; row info of this tile no longer needed
-    store_tile_lds(s_tile, v);
-    if (t + 1 < ntiles) tile_row_info(a.im, base + t0 + kTile, min((uint32_t)kTile, r1 - t0 - kTile), s_src, s_rot);
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(a.pool, s_src, min((uint32_t)kTile, r1 - t0 - kTile), v);
-
+  stream_tiles<kDepth>(a.im, a.im.rowmap, a.pool, a.pool_last, base + r0, r1 - r0, sm, [&](uint32_t, uint32_t nrows) {
+    f32x4_t acc[4];
+    qk_tile(sm.tile, qb, acc);
     float sc[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if ((uint32_t)(16 * j) < nrows) {
-        const f32x4_t acc = qk_block(s_tile, 16 * j, qb);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[j][i] = ((uint32_t)(16 * j + 4 * hq + i) < nrows) ? acc[i] * a.scale_log2 : -INFINITY;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[j][i] = -INFINITY;
-      }
-    }
+      for (int i = 0; i < 4; ++i)
+        sc[j][i] = ((uint32_t)(16 * j + 4 * hq + i) < nrows) ? acc[j][i] * a.scale_log2 : -INFINITY;
     float p[4][4];
     softmax_update_n<4, kNB>(sc, m, l, o, p);
-    pv_pair<kNB>(s_tile, 0, cg * kNB, pack_p8(p[0], p[1]), o);
-    if (nrows > 32) pv_pair<kNB>(s_tile, 32, cg * kNB, pack_p8(p[2], p[3]), o);
-  }
+    pv_pair<kNB>(sm.tile, 0, cg * kNB, pack_p8(p[0], p[1]), o);
+    if (nrows > 32) pv_pair<kNB>(sm.tile, 32, cg * kNB, pack_p8(p[2], p[3]), o);
+  });
 
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
@@ -583,14 +609,13 @@ struct PrefillArgs {
   uint16_t* out;
   float* lse;
   uint32_t n_q, n_heads, n_groups;
+  uint32_t pool_last;  // last valid pool row
   int32_t q_pos0;
   float scale_log2;
 };
 
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kTile * kLdsRow];
-  __shared__ uint32_t s_src[kTile];
-  __shared__ uint32_t s_rot[kTile];
+  __shared__ __attribute__((aligned(16))) TileSmem sm;
 
   const uint32_t g = blockIdx.x % a.n_groups;
   const uint32_t qblk = blockIdx.x / a.n_groups;
@@ -602,7 +627,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const uint32_t q_last = min(a.n_q, qblk * 4 + 4) - 1;
   const uint32_t rows = (uint32_t)a.q_pos0 + q_last + 1;   // KV rows this workgroup visits
   const int64_t lim = active ? (int64_t)a.q_pos0 + qi : -1;  // last visible row of this wave
-  const uint32_t base = a.im.seq_base[0];
 
   bf16x8_t qb[18];
   load_q(a.q_lat, a.q_rope, active ? qi : q_last, a.n_heads, head, qb);
@@ -611,40 +635,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  const uint32_t ntiles = (rows + kTile - 1) / kTile;
-  TileRegs v;
-  tile_row_info(a.im, base, min((uint32_t)kTile, rows), s_src, s_rot);
-  __syncthreads();
-  load_tile(a.pool, s_src, min((uint32_t)kTile, rows), v);
-  for (uint32_t t = 0; t < ntiles; ++t) {
-    const uint32_t t0 = t * kTile;
-    rotate_tile_regs(a.im.trig, s_rot, v);
-    __syncthreads();
-    store_tile_lds(s_tile, v);
-    if (t + 1 < ntiles) tile_row_info(a.im, base + t0 + kTile, min((uint32_t)kTile, rows - t0 - kTile), s_src, s_rot);
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(a.pool, s_src, min((uint32_t)kTile, rows - t0 - kTile), v);
+  stream_tiles<1>(a.im, a.im.rowmap, a.pool, a.pool_last, a.im.seq_base[0], rows, sm, [&](uint32_t t, uint32_t) {
+    const int64_t t0 = (int64_t)t * kTile;
+    if (t0 > lim) return;
+    f32x4_t acc[4];
+    qk_tile(sm.tile, qb, acc);
+    float sc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[j][i] = (t0 + 16 * j + 4 * hq + i <= lim) ? acc[j][i] * a.scale_log2 : -INFINITY;
+    float p[4][4];
+    softmax_update_n<4, 32>(sc, m, l, o, p);
+    pv_pair<32>(sm.tile, 0, 0, pack_p8(p[0], p[1]), o);
+    if (t0 + 32 <= lim) pv_pair<32>(sm.tile, 32, 0, pack_p8(p[2], p[3]), o);
+  });
 
-    if ((int64_t)t0 <= lim) {
-      f32x4_t acc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if ((int64_t)(t0 + 16 * j) <= lim) acc[j] = qk_block(s_tile, 16 * j, qb);
-        else acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-      float s[4][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s[j][i] = ((int64_t)(t0 + 16 * j + 4 * hq + i) <= lim) ? acc[j][i] * a.scale_log2 : -INFINITY;
-      i16x4_t pb[4];
-      softmax_update<4>(s, m, l, o, pb);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if ((int64_t)(t0 + 16 * j) <= lim) pv_block(s_tile, 16 * j, pb[j], o);
-    }
-  }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   if (!active) return;
@@ -744,6 +750,14 @@ extern "C" irm_status irm_table_upload(irm_table* t, const double* inv_freq, voi
                  "irm_table_upload: hipMemcpyAsync");
   if (st != IRM_OK) return st;
   t->dev = dev_buf;
+  if (t->total_rows) {
+    const uint32_t n = (uint32_t)t->total_rows;
+    const Image im = image_of(t);
+    hipLaunchKernelGGL(rowmap_kernel, dim3((n + 255) / 256), dim3(256), 0, s, im, n,
+                       const_cast<uint2*>(im.rowmap));
+    st = launch_check("irm_table_upload: row map kernel");
+    if (st != IRM_OK) { t->dev = nullptr; return st; }
+  }
   st = irm_table_set_rope(t, inv_freq, stream);
   if (st != IRM_OK) t->dev = nullptr;
   return st;
@@ -836,6 +850,7 @@ extern "C" irm_status irm_mla_decode(const void* q_latent, const void* q_rope, c
   a.n_seq = t->n_seq;
   a.n_heads = n_heads;
   a.n_splits = S;
+  a.pool_last = (uint32_t)((pool_rows < 0x100000000ull ? pool_rows : 0x100000000ull) - 1);
   a.scale_log2 = scale * kLog2e;
   // head groups per workgroup: 1 (4 column slices), 2 (2 slices) or 4 (full rows)
   const int hg = (int)heads_per_block(G);
@@ -845,11 +860,11 @@ extern "C" irm_status irm_mla_decode(const void* q_latent, const void* q_rope, c
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hg == 4)
-    hipLaunchKernelGGL((decode_split_kernel<4, 1>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<4, 1, kDecodeDepth>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   else if (hg == 2)
-    hipLaunchKernelGGL((decode_split_kernel<2, 2>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<2, 2, kDecodeDepth>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<1, 4>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<1, 4, kDecodeDepth>), dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   if ((st = launch_check("irm_mla_decode: split kernel")) != IRM_OK) return st;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(t->n_seq * n_heads), dim3(128), 0, s, a.ws_acc, a.ws_ml,
                      static_cast<uint16_t*>(out), lse, n_heads, S);
@@ -880,6 +895,7 @@ extern "C" irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_r
   a.lse = lse;
   a.n_q = n_q;
   a.n_heads = n_heads;
+  a.pool_last = (uint32_t)((pool_rows < 0x100000000ull ? pool_rows : 0x100000000ull) - 1);
   a.n_groups = n_heads / 16;
   a.q_pos0 = q_pos0;
   a.scale_log2 = scale * kLog2e;
