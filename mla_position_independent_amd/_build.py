@@ -32,6 +32,9 @@ def flags() -> list:
         "-shared",
         # packed-FP32 instructions are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators stay in arch VGPRs, where the online-softmax
+        # rescale works on them directly
+        "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
         "-Wall",
         f"-I{INCLUDE}",
         f"-I{CSRC}",

@@ -34,8 +34,8 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 
 // Device image: [entries | seq_first | seq_base | block_map | trig | rowmap].
 // The host copies everything before trig; trig (float2 cos/sin per entry and
-// pair) and the row map (uint2 {pool row, entry or ~0u if not rotated} per
-// assembled row) are computed on the GPU.
+// pair) and the row map (16-byte {pool row, delta, entry, 0} record per
+// assembled row, plus 64 records of padding) are computed on the GPU.
 struct ImageLayout {
   size_t off_entries = 0, off_seq_first = 0, off_seq_base = 0, off_block_map = 0;
   size_t off_trig = 0, off_rowmap = 0, bytes = 0;
@@ -55,6 +55,7 @@ struct irm_table {
   irm::ImageLayout layout;
   std::vector<unsigned char> image;  // host image of everything before trig
   void* dev = nullptr;               // device image after upload
+  double inv_freq[32] = {};          // RoPE frequencies of the last upload / set_rope
 };
 
 namespace irm {

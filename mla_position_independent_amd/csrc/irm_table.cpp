@@ -150,7 +150,7 @@ extern "C" irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunk
   L.off_seq_base = off;  off = irm::align_up(off + sizeof(uint32_t) * ((size_t)n_seq + 1));
   L.off_block_map = off; off = irm::align_up(off + sizeof(uint32_t) * t->block_map.size());
   L.off_trig = off;      off = irm::align_up(off + sizeof(float) * 2 * irm::kPairs * (size_t)n_chunks);
-  L.off_rowmap = off;    off = irm::align_up(off + sizeof(uint32_t) * 2 * (size_t)total);
+  L.off_rowmap = off;    off = irm::align_up(off + sizeof(uint32_t) * 4 * ((size_t)total + 64));
   L.bytes = off;
   t->image.assign(L.off_trig, 0);
   if (n_chunks)
