@@ -31,31 +31,95 @@ METRIC = "assembled KV tokens/s and MLA decode GB/s (% of HBM peak) vs CPU oracl
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 ROW_BYTES = 1152
-KERNEL_SOURCE = os.path.join(ROOT, "mla_position_independent_amd", "csrc", "irm_kernels.hip")
+CSRC = os.path.join(ROOT, "mla_position_independent_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# sources that define each timed kernel (a counter record is valid only for these bytes)
+KERNEL_SOURCES = {
+    "rotate_gather_kernel": ["irm_gather.hip", "irm_device.h"],
+    "decode_split_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
+    "prefill_kernel": ["irm_prefill.hip", "irm_attn.h", "irm_device.h"],
+}
 
 
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(key: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on the current source of that kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get(kernel)
-    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+    ent = rec.get(key)
+    kernel = key.split(":")[0]
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash(kernel):
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(path: str):
+    """(kernel name, counter name, value) of every dispatch in the rocprofv3
+    counter CSVs under path."""
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                                        recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                yield row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])
+
+
+def _mean_counter(path: str, counter: str, match) -> tuple:
+    vals = [v for k, c, v in _counter_rows(path) if c == counter and match(k)]
+    if not vals:
+        raise SystemExit(f"no {counter} values for the selected kernel under {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def ingest_counters(key: str, fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str):
+    """Turn two counter runs of a kernel (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) into HBM bytes per launch, each scaled by what the same counter
+    reads for a plain 1 GiB device copy, and record them in profiles/traffic.json."""
+    kernel = key.split(":")[0]
+    mk = lambda k: kernel in k
+    is_copy = lambda k: "copy" in k.lower() and "fill" not in k.lower()
+    copy_bytes = float(1 << 30)
+    f_kib, nf = _mean_counter(fetch_dir, "FETCH_SIZE", mk)
+    w_kib, nw = _mean_counter(write_dir, "WRITE_SIZE", mk)
+    cf_kib, _ = _mean_counter(cal_fetch_dir, "FETCH_SIZE", is_copy)
+    cw_kib, _ = _mean_counter(cal_write_dir, "WRITE_SIZE", is_copy)
+    f_scale = copy_bytes / (cf_kib * 1024.0)
+    w_scale = copy_bytes / (cw_kib * 1024.0)
+    fetch = f_kib * 1024.0 * f_scale
+    write = w_kib * 1024.0 * w_scale
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[key] = {"source_sha256_16": kernel_source_hash(kernel), "hbm_bytes_per_launch": round(fetch + write),
+                "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+                "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1), "dispatches": [nf, nw],
+                "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(cf_kib, 1), "write_kib": round(cw_kib, 1),
+                                     "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    log(f"{key}: fetch {fetch / 1e6:.1f} MB, write {write / 1e6:.1f} MB per launch -> {TRAFFIC_FILE}")
 
 
 def time_leg(fn, steps: int, warmup: int, inner_events: bool = True):
@@ -211,7 +275,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling HBM counters) and exit")
+    ap.add_argument("--profile", action="store_true",
+                    help="run the named legs only, without the JSON line or the CPU baseline")
+    ap.add_argument("--ingest-counters", nargs=5, metavar=("KEY", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="record rocprofv3 FETCH_SIZE/WRITE_SIZE runs of a kernel (scaled by the copy runs) "
+                         "in profiles/traffic.json and exit; KEY is e.g. rotate_gather_kernel")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by request "
               "or sequence with no exchange, and this build measures the one-GPU share.", file=sys.stderr)
@@ -237,10 +309,12 @@ def main():
         return
 
     legs = [x.strip() for x in args.legs.split(",") if x.strip()]
-    if "gather" not in legs:
+    if args.profile or "gather" not in legs:
         # profiling mode: run the requested legs only, no JSON line
         for name in legs:
-            if name == "decode":
+            if name == "gather":
+                leg_gather(args, irm, torch, synth)
+            elif name == "decode":
                 leg_decode(args, irm, torch, synth, "batched decode", synth.batched_decode)
             elif name == "long_decode":
                 leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)

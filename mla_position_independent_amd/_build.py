@@ -12,8 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libirm.so")
 
-SOURCES = ["irm_table.cpp", "irm_kernels.hip"]
-DEPS = SOURCES + ["irm_internal.h"]
+SOURCES = ["irm_table.cpp", "irm_abi.cpp", "irm_gather.hip", "irm_decode.hip", "irm_prefill.hip"]
+DEPS = SOURCES + ["irm_internal.h", "irm_device.h", "irm_attn.h", "irm_launch.h"]
 
 
 def hipcc() -> str:
