@@ -110,17 +110,24 @@ __device__ __forceinline__ void qk_blocks(const unsigned char* ckv, const unsign
   for (int i = 0; i < 2; ++i) krp[i] = kr + kr_pos(row0 + rr, 4 * i + q);
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 18; ++kk) {
-    bf16x8_t a[NB];
+  auto read = [&](int kk, bf16x8_t (&a)[NB]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const unsigned char* ptr = kk < 16 ? base[kk & 3] + 256 * (kk >> 2) + 16 * j * kCkvBytes
                                          : krp[kk - 16] + 16 * j * kKrBytes;
       a[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ptr));
     }
+  };
+  // double-buffered: the reads of step kk+1 are in flight while step kk's MFMAs run
+  bf16x8_t cur[NB], nxt[NB];
+  read(0, cur);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], qb[kk], acc[j], 0, 0, 0);
+  for (int kk = 0; kk < 18; ++kk) {
+    if (kk + 1 < 18) read(kk + 1, nxt);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[j], qb[kk], acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) cur[j] = nxt[j];
   }
 }
 
@@ -163,11 +170,43 @@ __device__ __forceinline__ void pv_block16(const unsigned char* st, uint32_t row
   for (int nb = 0; nb < NO; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v[nb], pb, o[nb], 0, 0, 0);
 }
 
-// Online softmax for one head per lane over NB blocks of 4 base-2 scores
-// (-inf where masked): updates m and the lane-local partial sum l, rescales o
-// when the maximum moved, and leaves the probabilities in p.
+// O^T += C^T P^T over a pair of 16-row blocks (rows row0.. and row0+16..) on
+// v_mfma_f32_16x16x32_bf16; the k order {4q..4q+3, 16+4q..16+4q+3} matches
+// the lane's probabilities of the two blocks, packed in pb.  Reads go out in
+// groups of eight column blocks, each group ahead of its MFMAs.
+template <int NO>
+__device__ __forceinline__ void pv_pair(const unsigned char* st, uint32_t row0, uint32_t nb0, bf16x8_t pb,
+                                        f32x4_t (&o)[NO]) {
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const CtBases c0 = ct_bases(st, row0);
+  constexpr int kGroup = NO < 8 ? NO : 8;
+#pragma unroll
+  for (int g0 = 0; g0 < NO; g0 += kGroup) {
+    i16x8_t v[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int nb = nb0 + g0 + j;
+      const i16x4_t lo = ct_read(c0, nb);
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_ptr)(c0.b[nb & 7] + 256 * (nb >> 3) + 16 * kCkvBytes));
+      v[j] = i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j)
+      o[g0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v[j]), pb, o[g0 + j], 0, 0, 0);
+  }
+}
+
+// Online softmax for one head per lane over NB blocks of 4 raw scores (-inf
+// where masked), in the base-2 domain: p = 2^(s c - m) with c = scale log2(e).
+// m is a reference maximum that moves only when a score exceeds it by more
+// than kSlack (or on the first finite score), so most tiles skip the rescale
+// of o; p then stays below 2^kSlack, harmless in bf16 and in the float sums.
+// Updates m, the lane-local partial sum l and o, and leaves p.
+constexpr float kSlack = 8.f;
+
 template <int NB, int NO>
-__device__ __forceinline__ void softmax_update_n(float (&s)[NB][4], float& m, float& l,
+__device__ __forceinline__ void softmax_update_n(const float (&s)[NB][4], float c, float& m, float& l,
                                                  f32x4_t (&o)[NO], float (&p)[NB][4]) {
   float mx = -INFINITY;
 #pragma unroll
@@ -176,23 +215,25 @@ __device__ __forceinline__ void softmax_update_n(float (&s)[NB][4], float& m, fl
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m, mx);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = exp2f(m - m_use);  // m == -inf gives 0
+  const float mxc = mx * c;  // -inf stays -inf (c > 0)
+  if (__any(mxc > m + kSlack)) {  // m == -inf takes this path on the first finite score
+    const float m_new = (mxc > m + kSlack) ? mxc : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 1 if unchanged, 0 from -inf
+    l *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NO; ++nb) o[nb] *= alpha;
+    m = m_new;
+  }
+  const float m_use = (m == -INFINITY) ? 0.f : m;
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[j][i] = exp2f(s[j][i] - m_use);
+      p[j][i] = __builtin_amdgcn_exp2f(fmaf(s[j][i], c, -m_use));
       sum += p[j][i];
     }
-  l = l * alpha + sum;
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int nb = 0; nb < NO; ++nb) o[nb] *= alpha;
-  }
-  m = m_new;
+  l += sum;
 }
 
 __device__ __forceinline__ i16x4_t pack_p4(const float (&a)[4]) {
@@ -208,6 +249,188 @@ __device__ __forceinline__ bf16x8_t pack_p8(const float (&a)[4], const float (&b
 
 __device__ __forceinline__ void fill_omega(double* omega, const InvFreq& f) {
   if (threadIdx.x < irm::kPairs) omega[threadIdx.x] = f.w[threadIdx.x];
+}
+
+// ---------------------------------------------------------------------------
+// Slices: R consecutive rows (R = 8 or 16) that one wave copies HBM -> LDS on
+// its own, placed at tile rows row0 .. row0+R-1 of a stage (the unit swizzle
+// depends on the tile row).  Per slice a wave issues one row-map copy (R
+// records of 16 B, lanes 0..R-1) and R + R/8 data copies (one 1 KB c_KV row
+// each, then the k_r of 8 rows per copy).
+// ---------------------------------------------------------------------------
+constexpr int kMaxSliceRows = 16;
+
+template <int kSlots>
+struct WaveSlots {
+  uint4 rm[kSlots][kMaxSliceRows];  // row-map records of prefetched slices
+  float2 trig[2][kPairs];           // (cos, sin) of all pairs for two deltas
+};
+
+// Row map of the slice whose first assembled row is g0, into rm.
+template <int R>
+__device__ __forceinline__ void slice_issue_rowmap(const StreamArgs& ra, uint32_t g0, uint4* rm) {
+  const uint32_t l = threadIdx.x & 63;
+  if (l < (uint32_t)R) dma16(ra.rowmap + g0 + l, lds_addr(rm));
+}
+
+// Data of the slice described by rec into tile rows row0.. of the stage with
+// c_KV at ckv and k_r at kr.  Pool rows are clamped so that a corrupted map
+// yields wrong values, never a fault.
+template <int R>
+__device__ __forceinline__ void slice_issue_data(const StreamArgs& ra, const uint4* rec, unsigned char* ckv,
+                                                 unsigned char* kr, uint32_t row0) {
+  const uint32_t l = opaque(threadIdx.x & 63);
+  uint32_t src[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) src[k] = min(rec[k].x, ra.pool_last);
+  uint32_t ksrc[R / 8];
+#pragma unroll
+  for (int h = 0; h < R / 8; ++h) ksrc[h] = min(rec[8 * h + (l >> 3)].x, ra.pool_last);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const uint32_t r = row0 + k;
+    dma16(ra.pool + (size_t)src[k] * kRowBytes + ((l ^ (r & 15)) << 4), lds_addr(ckv + r * kCkvBytes));
+  }
+#pragma unroll
+  for (int h = 0; h < R / 8; ++h) {
+    const uint32_t r = row0 + 8 * h + (l >> 3);
+    dma16(ra.pool + (size_t)ksrc[h] * kRowBytes + kCkvBytes + (((l & 7) ^ ((r >> 1) & 7)) << 4),
+          lds_addr(kr + (row0 + 8 * h) * kKrBytes));
+  }
+}
+
+// Rotate the k_r of a landed slice in place.  Lane l handles slice row
+// l / (64 / R) and R / 8 logical k_r units (4 pairs each); d is that row's
+// delta.  The wave keeps (cos, sin) of all 32 pairs for two deltas in LDS
+// (cd[0], cd[1]; 0 marks an empty slot, delta 0 needs no rotation).  Rows
+// whose delta is in the table rotate at once; otherwise a round evaluates
+// the table in double for two of the missing deltas (those of the first and
+// the last lane still waiting).  Deltas change only at entry boundaries, so
+// most slices need no round.  Nothing here touches global memory or scratch
+// (see dma16).
+template <int R, int kSlots>
+__device__ __forceinline__ void slice_rotate(WaveSlots<kSlots>& ws, unsigned char* kr, uint32_t row0,
+                                             const double* omega, int32_t d, int32_t (&cd)[2]) {
+  constexpr int kUnits = R / 8;  // units per lane
+  const uint32_t l = threadIdx.x & 63, r = row0 + l / (64 / R), u0 = kUnits * (l % (64 / R));
+  bool todo = d != 0;
+  while (__any(todo)) {
+    if (todo && (d == cd[0] || d == cd[1])) {
+      const f32x4_t* tp = reinterpret_cast<const f32x4_t*>(&ws.trig[d == cd[0] ? 0 : 1][4 * u0]);
+#pragma unroll
+      for (int h = 0; h < kUnits; ++h) {
+        const f32x4_t a = tp[2 * h], b = tp[2 * h + 1];
+        u32x4_t* p = reinterpret_cast<u32x4_t*>(kr + kr_pos(r, u0 + h));
+        const u32x4_t k = *p;
+        const u32x4_t o = {rotate_pair(k[0], a[0], a[1]), rotate_pair(k[1], a[2], a[3]),
+                           rotate_pair(k[2], b[0], b[1]), rotate_pair(k[3], b[2], b[3])};
+        *p = o;
+      }
+      todo = false;
+    }
+    const uint64_t mask = __ballot(todo);
+    if (mask == 0) break;
+    cd[0] = __shfl(d, __ffsll((unsigned long long)mask) - 1);
+    cd[1] = __shfl(d, 63 - __clzll((long long)mask));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // every lane is done with the old table
+    {
+      double sn, cn;
+      sincos((double)cd[l >> 5] * omega[l & 31], &sn, &cn);
+      ws.trig[l >> 5][l & 31] = make_float2((float)cn, (float)sn);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Delta of the slice row that lane l rotates.
+template <int R>
+__device__ __forceinline__ int32_t slice_row_delta(const uint4* rec) {
+  return (int32_t)rec[(threadIdx.x & 63) / (64 / R)].y;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_dma_but() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// ---------------------------------------------------------------------------
+// Shared 32-row tiles: four waves each copy and rotate one 8-row slice of
+// every tile into a four-stage LDS ring, and all four compute on the whole
+// tile.
+//
+// Iteration t: issue the data of tile t+3 into the stage tile t-1 left free
+// and the row map of tile t+6, compute tile t, wait until tile t+1 has
+// landed, rotate this wave's slice of tile t+1, barrier.  One barrier per
+// tile publishes tile t+1 and frees tile t's stage.  Copies per iteration
+// and wave: 9 data (only while tile t+3 exists) + 1 row map (always; past the
+// end it re-reads the last tile's records), so the wait for tile t+1 lets the
+// copies of iterations t-1 and t stay outstanding: 20, 11 or 2 of them.
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 32;
+constexpr int kStages = 4;
+constexpr int kTileSlice = kTileRows / 4;                       // rows per wave and tile
+constexpr int kTileRm = 8;                                      // row-map slots per wave
+constexpr int kTileKr = kTileRows * kCkvBytes;                  // k_r region of a stage
+constexpr int kTileBytes = kTileRows * (kCkvBytes + kKrBytes);  // 36864
+
+struct SharedSmem {
+  unsigned char stage[kStages][kTileBytes];
+  WaveSlots<kTileRm> slots[4];
+  double omega[kPairs];
+};
+
+// Wait until the data of tile x has landed, given which of tiles x+1, x+2
+// were issued after it (d1 implies d0's tile exists too).
+__device__ __forceinline__ void wait_tile(bool d1, bool d2) {
+  if (d2)
+    wait_dma_but<20>();
+  else if (d1)
+    wait_dma_but<11>();
+  else
+    wait_dma_but<2>();
+}
+
+// Stream assembled rows [g_begin, g_begin + n) and call compute(stage, t,
+// nrows) for every 32-row tile with its k_r rotated.  Every thread of the
+// workgroup calls this with the same arguments; sm.omega must be filled and
+// visible before the call.
+template <class Compute>
+__device__ __forceinline__ void shared_stream(const StreamArgs& ra, SharedSmem& sm, uint32_t g_begin, uint32_t n,
+                                              Compute&& compute) {
+  const uint32_t w = threadIdx.x >> 6;
+  const uint32_t nt = (n + kTileRows - 1) / kTileRows;
+  if (nt == 0) return;
+  WaveSlots<kTileRm>& ws = sm.slots[w];
+  const uint32_t row0 = kTileSlice * w;
+  int32_t cd[2] = {0, 0};
+  auto g0 = [&](uint32_t x) { return g_begin + min(x, nt - 1) * kTileRows + row0; };
+  auto issue = [&](uint32_t x) {  // data of tile x (if it exists) and row map of tile x+3
+    if (x < nt) slice_issue_data<kTileSlice>(ra, ws.rm[x % kTileRm], sm.stage[x % kStages],
+                                             sm.stage[x % kStages] + kTileKr, row0);
+    slice_issue_rowmap<kTileSlice>(ra, g0(x + 3), ws.rm[(x + 3) % kTileRm]);
+  };
+  auto rotate = [&](uint32_t x) {
+    slice_rotate<kTileSlice>(ws, sm.stage[x % kStages] + kTileKr, row0, sm.omega,
+                             slice_row_delta<kTileSlice>(ws.rm[x % kTileRm]), cd);
+  };
+
+  for (uint32_t x = 0; x < 3; ++x) slice_issue_rowmap<kTileSlice>(ra, g0(x), ws.rm[x]);
+  wait_dma_all();
+  for (uint32_t x = 0; x < 3; ++x) issue(x);
+  wait_tile(1 < nt, 2 < nt);
+  rotate(0);
+  __syncthreads();
+  for (uint32_t t = 0; t < nt; ++t) {
+    issue(t + 3);
+    compute(static_cast<const unsigned char*>(sm.stage[t % kStages]), t, min((uint32_t)kTileRows, n - t * kTileRows));
+    if (t + 1 < nt) {
+      wait_tile(t + 2 < nt, t + 3 < nt);
+      rotate(t + 1);
+    }
+    __syncthreads();
+  }
+  wait_dma_all();
 }
 
 }  // namespace dev

@@ -17,116 +17,6 @@ namespace {
 
 using namespace irm::dev;
 
-// ---------------------------------------------------------------------------
-// split-KV decode, pass 1: wave-private KV streams
-//
-// Workgroup = (sequence, split, 16-head group), 4 waves, one workgroup per
-// CU.  The split's rows are cut into four contiguous ranges, one per wave,
-// and every wave streams its range on its own: 16-row tiles are copied
-// HBM -> LDS into a private two-stage ring (global_load_lds_dwordx4), k_r is
-// rotated in place, and the wave scores the 16 rows for its 16 heads and
-// accumulates all 512 output columns.  Nothing in the tile loop waits for
-// another wave; the four online-softmax states merge once at the end.
-//
-// Per iteration t a wave issues the row map of tile t+3 (one copy) and the
-// data of tile t+1 (16 c_KV rows + 2 k_r copies), then waits until at most
-// those 19 copies are outstanding, which means tile t has landed.
-// ---------------------------------------------------------------------------
-constexpr int kWaveRows = 16;
-constexpr int kWaveRm = 4;                                          // row-map slots
-constexpr int kWaveStageKr = kWaveRows * kCkvBytes;                 // k_r region of a stage
-constexpr int kWaveStageBytes = kWaveRows * (kCkvBytes + kKrBytes); // 18432
-constexpr int kWaveCopies = 1 + kWaveRows + 2;                      // copies per iteration
-
-struct WaveRing {
-  unsigned char stage[2][kWaveStageBytes];
-  uint4 rm[kWaveRm][kWaveRows];  // row-map records
-  float2 trig[2][irm::kPairs];   // (cos, sin) for two deltas
-};
-
-struct DecodeSmem {
-  WaveRing w[kThreads / 64];
-  double omega[irm::kPairs];
-  float ml[kThreads / 64][16][2];
-};
-
-__device__ __forceinline__ void wave_wait_tile() { asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); }
-__device__ __forceinline__ void wave_wait_rm() { asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); }
-static_assert(kWaveCopies == 19, "the wave wait counts one iteration's copies");
-
-struct WaveRange {
-  uint32_t g_begin, n, ntiles;
-  __device__ uint32_t g0(uint32_t x) const { return g_begin + min(x, ntiles - 1) * kWaveRows; }
-};
-
-// Row map of tile x (16 records of 16 B, one per lane 0..15); x is clamped to the last tile.
-__device__ __forceinline__ void wave_issue_rowmap(const StreamArgs& ra, const WaveRange& wr, WaveRing& wv, uint32_t x) {
-  const uint32_t l = threadIdx.x & 63;
-  if (l < kWaveRows) dma16(ra.rowmap + wr.g0(x) + l, lds_addr(&wv.rm[x % kWaveRm][0]));
-}
-
-// Data of tile x: one 1 KB c_KV row per copy, then k_r of rows 0-7 and 8-15.
-// Pool rows are clamped so that a corrupted map yields wrong values, not a fault.
-__device__ __forceinline__ void wave_issue_data(const StreamArgs& ra, WaveRing& wv, uint32_t x) {
-  const uint32_t l = opaque(threadIdx.x & 63);
-  unsigned char* st = wv.stage[x & 1];
-  const uint4* rec = wv.rm[x % kWaveRm];
-  uint32_t src[kWaveRows];
-#pragma unroll
-  for (int r = 0; r < kWaveRows; ++r) src[r] = min(rec[r].x, ra.pool_last);
-  const uint32_t kr0 = min(rec[l >> 3].x, ra.pool_last), kr1 = min(rec[8 + (l >> 3)].x, ra.pool_last);
-#pragma unroll
-  for (int r = 0; r < kWaveRows; ++r)
-    dma16(ra.pool + (size_t)src[r] * kRowBytes + ((l ^ r) << 4), lds_addr(st + r * kCkvBytes));
-  const uint32_t r0 = l >> 3, r1 = 8 + (l >> 3);
-  dma16(ra.pool + (size_t)kr0 * kRowBytes + kCkvBytes + (((l & 7) ^ ((r0 >> 1) & 7)) << 4),
-        lds_addr(st + kWaveStageKr));
-  dma16(ra.pool + (size_t)kr1 * kRowBytes + kCkvBytes + (((l & 7) ^ ((r1 >> 1) & 7)) << 4),
-        lds_addr(st + kWaveStageKr + 8 * kKrBytes));
-}
-
-// Rotate the k_r of a landed tile in place.  Lane l handles row l/4 and the
-// logical k_r units 2 (l%4) and 2 (l%4) + 1, i.e. pairs 8 (l%4) .. +7.  The
-// wave keeps (cos, sin) of all 32 pairs for two deltas in LDS (cd[0], cd[1];
-// 0 marks an empty slot, delta 0 needs no rotation).  Rows whose delta is in
-// the table rotate at once; otherwise a round evaluates the table for two of
-// the missing deltas (those of the first and the last lane still waiting).
-// Deltas change only at entry boundaries, so most tiles need no round.
-__device__ __forceinline__ void wave_rotate(WaveRing& wv, unsigned char* st, const double* omega, int32_t d,
-                                            int32_t (&cd)[2]) {
-  const uint32_t l = threadIdx.x & 63, r = l >> 2, u0 = 2 * (l & 3);
-  bool todo = d != 0;
-  while (__any(todo)) {
-    if (todo && (d == cd[0] || d == cd[1])) {
-      const f32x4_t* tp = reinterpret_cast<const f32x4_t*>(&wv.trig[d == cd[0] ? 0 : 1][8 * (l & 3)]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4_t a = tp[2 * h], b = tp[2 * h + 1];
-        u32x4_t* p = reinterpret_cast<u32x4_t*>(st + kWaveStageKr + kr_pos(r, u0 + h));
-        const u32x4_t k = *p;
-        const u32x4_t o = {rotate_pair(k[0], a[0], a[1]), rotate_pair(k[1], a[2], a[3]),
-                           rotate_pair(k[2], b[0], b[1]), rotate_pair(k[3], b[2], b[3])};
-        *p = o;
-      }
-      todo = false;
-    }
-    const uint64_t mask = __ballot(todo);
-    if (mask == 0) break;
-    cd[0] = __shfl(d, __ffsll((unsigned long long)mask) - 1);
-    cd[1] = __shfl(d, 63 - __clzll((long long)mask));
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // every lane is done with the old table
-    {
-      double sn, cn;
-      sincos((double)cd[l >> 5] * omega[l & 31], &sn, &cn);
-      wv.trig[l >> 5][l & 31] = make_float2((float)cn, (float)sn);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-}
-
 struct DecodeArgs {
   StreamArgs ra;
   const uint32_t* seq_base;
@@ -139,8 +29,64 @@ struct DecodeArgs {
   InvFreq f;
 };
 
-__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) DecodeSmem sm;
+// Rows [r0, r1) of the split sp of a sequence with N rows: splits are whole
+// multiples of 64 rows so that every wave range and tile is aligned.
+__device__ __forceinline__ void split_rows(uint32_t N, uint32_t n_splits, uint32_t sp, uint32_t& r0, uint32_t& r1) {
+  const uint32_t per = ((N + n_splits - 1) / n_splits + 63) / 64 * 64;
+  r0 = min(N, sp * per);
+  r1 = min(N, r0 + per);
+}
+
+// Raw scores of one 16-row block for 16 heads, -inf from row nvalid on.
+__device__ __forceinline__ void mask_rows(const f32x4_t& acc, uint32_t row0, uint32_t nvalid, float (&sc)[4]) {
+  const uint32_t hq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] = (row0 + 4 * hq + i < nvalid) ? acc[i] : -INFINITY;
+}
+
+// Write one wave's softmax state for its 16 heads (lane (hq, hr) holds head
+// hr, columns 16 nb + 4 hq + i) into the split's workspace slot.
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, size_t pidx, float m, float l, const f32x4_t (&o)[32]) {
+  const uint32_t lane = threadIdx.x & 63, hq = lane >> 4, hr = lane & 15;
+  float* dst = a.ws_acc + (pidx + hr) * IRM_D_LATENT + 4 * hq;
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb)
+    *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[nb][0], o[nb][1], o[nb][2], o[nb][3]);
+  if (hq == 0) {
+    a.ws_ml[(pidx + hr) * 2 + 0] = m;
+    a.ws_ml[(pidx + hr) * 2 + 1] = (m == -INFINITY) ? 0.f : l;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split-KV decode, pass 1, one 16-head group per workgroup: wave-private
+// streams
+//
+// Workgroup = (sequence, split, 16-head group), 4 waves, one workgroup per
+// CU.  The split's rows are cut into four contiguous ranges, one per wave,
+// and every wave streams its range on its own in 16-row slices through a
+// private two-stage LDS ring, rotates k_r in place, scores the 16 rows for
+// its 16 heads and accumulates all 512 output columns.  Nothing in the slice
+// loop waits for another wave; the four online-softmax states merge once at
+// the end.  Per iteration t a wave issues the row map of slice t+3 and the
+// data of slice t+1, then waits until at most those 19 copies are
+// outstanding, which means slice t has landed.
+// ---------------------------------------------------------------------------
+constexpr int kPrivRows = 16;
+constexpr int kPrivStageKr = kPrivRows * kCkvBytes;
+constexpr int kPrivStageBytes = kPrivRows * (kCkvBytes + kKrBytes);  // 18432
+
+constexpr int kPrivRm = 4;  // row-map slots per wave
+
+struct PrivateSmem {
+  unsigned char stage[4][2][kPrivStageBytes];
+  WaveSlots<kPrivRm> slots[4];
+  double omega[kPairs];
+  float ml[4][16][2];
+};
+
+__global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) PrivateSmem sm;
 
   // Workgroups of the same (sequence, split) but different head groups get
   // the same x % 8, i.e. the same XCD and L2, at consecutive slots.
@@ -151,22 +97,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   const uint32_t b = bs / a.n_splits, sp = bs % a.n_splits;
 
   const uint32_t base = a.seq_base[b];
-  const uint32_t N = a.seq_base[b + 1] - base;
-  const uint32_t per = ((N + a.n_splits - 1) / a.n_splits + 63) / 64 * 64;
-  const uint32_t r0 = min(N, sp * per), r1 = min(N, r0 + per);
+  uint32_t r0, r1;
+  split_rows(a.seq_base[b + 1] - base, a.n_splits, sp, r0, r1);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hq = lane >> 4, hr = lane & 15;
   const uint32_t head = g * 16 + hr;
 
-  // this wave's rows: a quarter of the split, in whole tiles
-  const uint32_t quarter = ((r1 - r0 + 3) / 4 + kWaveRows - 1) / kWaveRows * kWaveRows;
+  // this wave's rows: a quarter of the split, in whole slices
+  const uint32_t quarter = ((r1 - r0 + 3) / 4 + kPrivRows - 1) / kPrivRows * kPrivRows;
   const uint32_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
-  WaveRange wr;
-  wr.g_begin = base + w0;
-  wr.n = w1 - w0;
-  wr.ntiles = (wr.n + kWaveRows - 1) / kWaveRows;
-  WaveRing& wv = sm.w[wave];
+  const uint32_t g_begin = base + w0, n = w1 - w0;
+  const uint32_t nt = (n + kPrivRows - 1) / kPrivRows;
+  WaveSlots<kPrivRm>& ws = sm.slots[wave];
+  auto g0 = [&](uint32_t t) { return g_begin + min(t, nt - 1) * kPrivRows; };
 
   bf16x8_t qb[18];
   load_q(a.q_lat, a.q_rope, b, a.n_heads, head, qb);
@@ -178,30 +122,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   int32_t cd[2] = {0, 0};  // deltas held in the wave's trig table
   __syncthreads();
 
-  if (wr.ntiles > 0) {
-    for (uint32_t t = 0; t < 3; ++t) wave_issue_rowmap(a.ra, wr, wv, t);
+  if (nt > 0) {
+    for (uint32_t t = 0; t < 3; ++t) slice_issue_rowmap<kPrivRows>(a.ra, g0(t), ws.rm[t]);
     wait_dma_all();
-    wave_issue_data(a.ra, wv, 0);
-    for (uint32_t t = 0; t < wr.ntiles; ++t) {
+    slice_issue_data<kPrivRows>(a.ra, ws.rm[0], sm.stage[wave][0], sm.stage[wave][0] + kPrivStageKr, 0);
+    for (uint32_t t = 0; t < nt; ++t) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of the stage about to be refilled are done
-      wave_issue_rowmap(a.ra, wr, wv, t + 3);
-      if (t + 1 < wr.ntiles) {
-        wave_issue_data(a.ra, wv, t + 1);
-        wave_wait_tile();
+      slice_issue_rowmap<kPrivRows>(a.ra, g0(t + 3), ws.rm[(t + 3) % kPrivRm]);
+      if (t + 1 < nt) {
+        unsigned char* nx = sm.stage[wave][(t + 1) & 1];
+        slice_issue_data<kPrivRows>(a.ra, ws.rm[(t + 1) % kPrivRm], nx, nx + kPrivStageKr, 0);
+        wait_dma_but<19>();
       } else {
-        wave_wait_rm();
+        wait_dma_but<1>();
       }
-      unsigned char* st = wv.stage[t & 1];
-      const uint32_t nrows = min((uint32_t)kWaveRows, wr.n - t * kWaveRows);
-      const int32_t d = (int32_t)wv.rm[t % kWaveRm][lane >> 2].y;
-      wave_rotate(wv, st, sm.omega, d, cd);
+      unsigned char* st = sm.stage[wave][t & 1];
+      slice_rotate<kPrivRows>(ws, st + kPrivStageKr, 0, sm.omega, slice_row_delta<kPrivRows>(ws.rm[t % kPrivRm]), cd);
       f32x4_t acc[1];
-      qk_blocks<1>(st, st + kWaveStageKr, 0, qb, acc);
-      float sc[1][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[0][i] = (4 * hq + i < (int)nrows) ? acc[0][i] * a.scale_log2 : -INFINITY;
+      qk_blocks<1>(st, st + kPrivStageKr, 0, qb, acc);
+      float sc[1][4] = {{acc[0][0], acc[0][1], acc[0][2], acc[0][3]}};
+      const uint32_t nv = n - t * kPrivRows;
+      if (nv < (uint32_t)kPrivRows) mask_rows(acc[0], 0, nv, sc[0]);
       float p[1][4];
-      softmax_update_n<1, 32>(sc, m, l, o, p);
+      softmax_update_n<1, 32>(sc, a.scale_log2, m, l, o, p);
       pv_block16<32>(st, 0, 0, pack_p4(p[0]), o);
     }
     wait_dma_all();  // the last row-map copies
@@ -226,8 +169,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     lsum += sm.ml[w][hr][1] * f;
     if (w == wave) fw = f;
   }
-  float* red = reinterpret_cast<float*>(&sm.w[0].stage[0][0]);  // [4 waves][16 heads][512]
-  static_assert(4 * 16 * IRM_D_LATENT * 4 <= 4 * sizeof(WaveRing), "merge buffer fits the rings");
+  float* red = reinterpret_cast<float*>(&sm.stage[0][0][0]);  // [4 waves][16 heads][512]
+  static_assert(4 * 16 * IRM_D_LATENT * 4 <= sizeof(sm.stage), "merge buffer fits the rings");
   float* mine = red + wave * 16 * IRM_D_LATENT;
 #pragma unroll
   for (int nb = 0; nb < 32; ++nb) {
@@ -251,7 +194,66 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// split-KV decode, pass 2: merge the splits of each (sequence, head)
+// split-KV decode, pass 1, four 16-head groups per workgroup: shared tiles
+//
+// Workgroup = (sequence, split, 64-head block); wave w owns head group
+// 4 blk + w.  All four waves read every tile of the split, so the KV
+// is copied once per 64 heads instead of once per 16; each wave copies and
+// rotates one 8-row slice of every 32-row tile (shared_stream).  A wave's partial
+// state goes straight to the workspace: the waves hold different heads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void decode_shared_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) SharedSmem sm;
+
+  const uint32_t n_blk = a.n_groups / 4;
+  const uint32_t x = blockIdx.x, xcd = x & 7, slot = x >> 3;
+  const uint32_t hb = slot % n_blk;
+  const uint32_t bs = (slot / n_blk) * 8 + xcd;
+  if (bs >= a.n_seq * a.n_splits) return;
+  const uint32_t b = bs / a.n_splits, sp = bs % a.n_splits;
+
+  const uint32_t base = a.seq_base[b];
+  uint32_t r0, r1;
+  split_rows(a.seq_base[b + 1] - base, a.n_splits, sp, r0, r1);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hr = lane & 15;
+  const uint32_t g = hb * 4 + wave;
+  const uint32_t head = g * 16 + hr;
+
+  bf16x8_t qb[18];
+  load_q(a.q_lat, a.q_rope, b, a.n_heads, head, qb);
+  fill_omega(sm.omega, a.f);
+  f32x4_t o[32];
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  __syncthreads();
+
+  shared_stream(a.ra, sm, base + r0, r1 - r0, [&](const unsigned char* st, uint32_t, uint32_t nrows) {
+    f32x4_t acc[2];
+    qk_blocks<2>(st, st + kTileKr, 0, qb, acc);
+    float sc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[j][i] = acc[j][i];
+    if (nrows < (uint32_t)kTileRows) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mask_rows(acc[j], 16 * j, nrows, sc[j]);
+    }
+    float p[2][4];
+    softmax_update_n<2, 32>(sc, a.scale_log2, m, l, o, p);
+    pv_pair<32>(st, 0, 0, pack_p8(p[0], p[1]), o);
+  });
+
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  store_partial(a, ((size_t)b * a.n_splits + sp) * a.n_heads + g * 16, m, l, o);
+}
+
+// ---------------------------------------------------------------------------
+// split-KV decode, pass 2
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws_acc,
                                                              const float* __restrict__ ws_ml,
@@ -296,8 +298,10 @@ StreamArgs stream_args(const irm_table* t, const void* pool, uint64_t pool_rows)
 }  // namespace
 
 uint32_t decode_default_splits(const irm_table* t, uint32_t n_groups) {
-  // one workgroup per CU (256 CUs) with >= 256 rows per split
-  const uint32_t want = (256 + t->n_seq * n_groups - 1) / (t->n_seq * n_groups);
+  // one workgroup per CU (256 CUs) with >= 256 rows per split; a workgroup
+  // covers four head groups when the head count allows it
+  const uint32_t units = (n_groups % 4 == 0) ? n_groups / 4 : n_groups;
+  const uint32_t want = (256 + t->n_seq * units - 1) / (t->n_seq * units);
   const uint32_t cap = (t->max_seq_len + 255) / 256;
   uint32_t s = want < cap ? want : cap;
   if (s < 1) s = 1;
@@ -322,10 +326,14 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
   a.n_splits = n_splits;
   a.scale_log2 = scale * kLog2e;
   for (int i = 0; i < (int)kPairs; ++i) a.f.w[i] = t->inv_freq[i];
+  const bool shared = G % 4 == 0;
   const uint64_t bs = (uint64_t)t->n_seq * n_splits;
-  const uint64_t grid = (bs + 7) / 8 * 8 * G;
+  const uint64_t grid = (bs + 7) / 8 * 8 * (shared ? G / 4 : G);
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");
-  hipLaunchKernelGGL(decode_split_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+  if (shared)
+    hipLaunchKernelGGL(decode_shared_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_private_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   irm_status st = launch_check("irm_mla_decode: split kernel");
   if (st != IRM_OK) return st;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(t->n_seq * n_heads), dim3(128), 0, s, ws_acc, ws_ml,
