@@ -23,28 +23,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libirm.so)")
 
 
+# Sources whose MFMA accumulators stay in arch VGPRs, where the online-softmax
+# rescale works on them directly (Q operands are kept in AGPRs instead).
+VGPR_FORM = {"irm_decode.hip", "irm_gather.hip", "irm_prefill.hip"}
+
+
 def flags() -> list:
     return [
         "--offload-arch=gfx950",
         "-O3",
         "-std=c++17",
         "-fPIC",
-        "-shared",
         # packed-FP32 instructions are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators stay in arch VGPRs, where the online-softmax
-        # rescale works on them directly
-        "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
         "-Wall",
         f"-I{INCLUDE}",
         f"-I{CSRC}",
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into mla_position_independent_amd/libirm.so."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + flags() + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def source_flags(name: str) -> list:
+    extra = ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"] if name in VGPR_FORM else []
+    return flags() + extra
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,8 +57,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+
+
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> str:
+    """Compile every source (each with its own flags) and link libirm.so."""
+    objdir = os.path.join(os.path.dirname(out), "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for s in SOURCES:
+        obj = os.path.join(objdir, s + ".o")
+        inc = [] if csrc == CSRC else [f"-I{csrc}"]
+        _run([hipcc()] + inc + source_flags(s) + ["-c", os.path.join(csrc, s), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = out + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

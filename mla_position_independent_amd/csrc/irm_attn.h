@@ -75,6 +75,7 @@ struct StreamArgs {
 
 // Q^T operands of 16 heads for one query: lane (q, r) holds head head0 + r,
 // dims 32 kk + 8 q .. +8 (kk 0..15 latent, 16..17 rope).
+template <bool kInAgpr = true>
 __device__ __forceinline__ void load_q(const uint4* __restrict__ q_lat, const uint4* __restrict__ q_rope,
                                        uint32_t qrow, uint32_t n_heads, uint32_t head,
                                        bf16x8_t (&qb)[18]) {
@@ -85,11 +86,17 @@ __device__ __forceinline__ void load_q(const uint4* __restrict__ q_lat, const ui
   for (int kk = 0; kk < 16; ++kk) qb[kk] = __builtin_bit_cast(bf16x8_t, pl[4 * kk]);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) qb[16 + kk] = __builtin_bit_cast(bf16x8_t, pr[4 * kk]);
-  // Consume the loads here: the tile loop below issues LDS copies the
-  // compiler cannot see, and a wait for these loads inside the loop would
-  // also wait for those copies.
+  // Consume the loads here: the tile loop issues LDS copies the compiler
+  // cannot see, and a wait for these loads inside the loop would also wait
+  // for those copies.  The operands then stay in the register file asked for
+  // (MFMA reads its B operand from either).
 #pragma unroll
-  for (int kk = 0; kk < 18; ++kk) asm volatile("" : "+a"(qb[kk]));
+  for (int kk = 0; kk < 18; ++kk) {
+    if constexpr (kInAgpr)
+      asm volatile("" : "+a"(qb[kk]));
+    else
+      asm volatile("" : "+v"(qb[kk]));
+  }
 }
 
 // Scores of NB 16-row blocks starting at row0 (a multiple of 16), blocks
@@ -258,12 +265,10 @@ __device__ __forceinline__ void fill_omega(double* omega, const InvFreq& f) {
 // records of 16 B, lanes 0..R-1) and R + R/8 data copies (one 1 KB c_KV row
 // each, then the k_r of 8 rows per copy).
 // ---------------------------------------------------------------------------
-constexpr int kMaxSliceRows = 16;
-
-template <int kSlots>
+template <int kSlots, int R>
 struct WaveSlots {
-  uint4 rm[kSlots][kMaxSliceRows];  // row-map records of prefetched slices
-  float2 trig[2][kPairs];           // (cos, sin) of all pairs for two deltas
+  uint4 rm[kSlots][R];     // row-map records of prefetched slices
+  float2 trig[2][kPairs];  // (cos, sin) of all pairs for two deltas
 };
 
 // Row map of the slice whose first assembled row is g0, into rm.
@@ -309,7 +314,7 @@ __device__ __forceinline__ void slice_issue_data(const StreamArgs& ra, const uin
 // most slices need no round.  Nothing here touches global memory or scratch
 // (see dma16).
 template <int R, int kSlots>
-__device__ __forceinline__ void slice_rotate(WaveSlots<kSlots>& ws, unsigned char* kr, uint32_t row0,
+__device__ __forceinline__ void slice_rotate(WaveSlots<kSlots, R>& ws, unsigned char* kr, uint32_t row0,
                                              const double* omega, int32_t d, int32_t (&cd)[2]) {
   constexpr int kUnits = R / 8;  // units per lane
   const uint32_t l = threadIdx.x & 63, r = row0 + l / (64 / R), u0 = kUnits * (l % (64 / R));
@@ -376,7 +381,7 @@ constexpr int kTileBytes = kTileRows * (kCkvBytes + kKrBytes);  // 36864
 
 struct SharedSmem {
   unsigned char stage[kStages][kTileBytes];
-  WaveSlots<kTileRm> slots[4];
+  WaveSlots<kTileRm, kTileSlice> slots[4];
   double omega[kPairs];
 };
 
@@ -401,7 +406,7 @@ __device__ __forceinline__ void shared_stream(const StreamArgs& ra, SharedSmem& 
   const uint32_t w = threadIdx.x >> 6;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
-  WaveSlots<kTileRm>& ws = sm.slots[w];
+  WaveSlots<kTileRm, kTileSlice>& ws = sm.slots[w];
   const uint32_t row0 = kTileSlice * w;
   int32_t cd[2] = {0, 0};
   auto g0 = [&](uint32_t x) { return g_begin + min(x, nt - 1) * kTileRows + row0; };
@@ -431,6 +436,143 @@ __device__ __forceinline__ void shared_stream(const StreamArgs& ra, SharedSmem& 
     __syncthreads();
   }
   wait_dma_all();
+}
+
+// ---------------------------------------------------------------------------
+// Split tiles: four groups of 16 query-heads per workgroup, output columns
+// split across the waves
+//
+// Each 32-row tile serves four groups of 16 query-heads (four queries of one
+// head group in prefill, four head groups of one query in decode).  Wave w
+// scores group w (K fragments from LDS, Q in registers), runs its online
+// softmax, and publishes the probabilities (already in the lane layout of
+// the PV B operand) and any rescale factors through LDS.  After a barrier,
+// wave w accumulates O for all four groups over output columns
+// 128 w .. 128 w + 127, so every C^T fragment it reads feeds four MFMAs.
+// Per tile and wave: 36 + 32 MFMAs; LDS reads 36 KB (K) + 8 KB (C^T) + 4 KB
+// (P), against 36 KB + 32 KB when every wave accumulates all columns of its
+// own group.
+// ---------------------------------------------------------------------------
+constexpr int kSplitGroups = 4;
+constexpr int kSplitCols = IRM_D_LATENT / kSplitGroups;  // 128 output columns per wave
+constexpr int kSplitNb = kSplitCols / 16;                // 8 column blocks
+
+struct SplitSmem {
+  SharedSmem s;
+  uint4 pfrag[kSplitGroups][64];  // P^T operand of group g for lane l (8 bf16)
+  float alpha[kSplitGroups][16];  // rescale factor of group g, head l % 16
+  uint32_t scaled[kSplitGroups];  // group g moved its reference maximum on this tile
+  float ml[kSplitGroups][16][2];  // final (m, l) of group g, head l % 16
+};
+static_assert(sizeof(SplitSmem) <= 160 * 1024, "split tiles fit the LDS");
+
+// Online softmax of one group over 2 blocks of 4 raw scores per lane (-inf
+// where masked), without touching O: leaves p, returns alpha (1 if the
+// reference maximum did not move) and whether any head moved it.
+__device__ __forceinline__ bool softmax_scores(const float (&s)[2][4], float c, float& m, float& l,
+                                               float (&p)[2][4], float& alpha) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mxc = mx * c;
+  alpha = 1.f;
+  const bool moved = __any(mxc > m + kSlack);
+  if (moved) {
+    const float m_new = (mxc > m + kSlack) ? mxc : m;
+    alpha = __builtin_amdgcn_exp2f(m - m_new);
+    l *= alpha;
+    m = m_new;
+  }
+  const float m_use = (m == -INFINITY) ? 0.f : m;
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[j][i] = __builtin_amdgcn_exp2f(fmaf(s[j][i], c, -m_use));
+      sum += p[j][i];
+    }
+  l += sum;
+  return moved;
+}
+
+// One 32-row tile.  last is the last visible tile row of the wave's own group
+// (>= 31: the whole tile; < 0: none of it).
+__device__ __forceinline__ void split_tile(SplitSmem& sm, const unsigned char* st, float c, int32_t last,
+                                           const bf16x8_t (&qb)[18], float& m, float& l,
+                                           f32x4_t (&o)[kSplitGroups][kSplitNb]) {
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = lane >> 4, hr = lane & 15;
+  // phase A: scores, softmax and P of group w
+  {
+    f32x4_t acc[2];
+    qk_blocks<2>(st, st + kTileKr, 0, qb, acc);
+    float sc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[j][i] = acc[j][i];
+    if (last < kTileRows - 1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((int32_t)(16 * j + 4 * hq + i) > last) sc[j][i] = -INFINITY;
+    }
+    float p[2][4], alpha;
+    const bool moved = softmax_scores(sc, c, m, l, p, alpha);
+    sm.pfrag[w][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
+    if (hq == 0) sm.alpha[w][hr] = alpha;
+    if (lane == 0) sm.scaled[w] = moved ? 1u : 0u;
+  }
+  __syncthreads();
+  // phase B: O of the four groups over this wave's columns
+  {
+#pragma unroll
+    for (int g = 0; g < kSplitGroups; ++g) {
+      if (sm.scaled[g]) {
+        const float a = sm.alpha[g][hr];
+#pragma unroll
+        for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] *= a;
+      }
+    }
+    bf16x8_t pf[kSplitGroups];
+#pragma unroll
+    for (int g = 0; g < kSplitGroups; ++g) pf[g] = __builtin_bit_cast(bf16x8_t, sm.pfrag[g][lane]);
+    typedef short i16x8_t __attribute__((ext_vector_type(8)));
+    const CtBases c0 = ct_bases(st, 0);
+    auto cread = [&](int nb) {
+      const int n = kSplitNb * w + nb;
+      const i16x4_t lo = ct_read(c0, n);
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_ptr)(c0.b[n & 7] + 256 * (n >> 3) + 16 * kCkvBytes));
+      return __builtin_bit_cast(bf16x8_t, (i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
+    };
+    bf16x8_t cf[kSplitNb];
+#pragma unroll
+    for (int nb = 0; nb < kSplitNb; ++nb) cf[nb] = cread(nb);
+#pragma unroll
+    for (int nb = 0; nb < kSplitNb; ++nb)
+#pragma unroll
+      for (int g = 0; g < kSplitGroups; ++g)
+        o[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[nb], pf[g], o[g][nb], 0, 0, 0);
+  }
+}
+
+// Owners publish (m, l) of their group; after this every wave can normalise
+// its columns of all four groups.  l is reduced over the lane quarters here.
+__device__ __forceinline__ void split_publish(SplitSmem& sm, float m, float l) {
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if ((lane >> 4) == 0) {
+    sm.ml[w][lane & 15][0] = m;
+    sm.ml[w][lane & 15][1] = l;
+  }
+  __syncthreads();
 }
 
 }  // namespace dev

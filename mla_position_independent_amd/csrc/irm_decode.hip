@@ -80,7 +80,7 @@ constexpr int kPrivRm = 4;  // row-map slots per wave
 
 struct PrivateSmem {
   unsigned char stage[4][2][kPrivStageBytes];
-  WaveSlots<kPrivRm> slots[4];
+  WaveSlots<kPrivRm, kPrivRows> slots[4];
   double omega[kPairs];
   float ml[4][16][2];
 };
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
   const uint32_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
   const uint32_t g_begin = base + w0, n = w1 - w0;
   const uint32_t nt = (n + kPrivRows - 1) / kPrivRows;
-  WaveSlots<kPrivRm>& ws = sm.slots[wave];
+  WaveSlots<kPrivRm, kPrivRows>& ws = sm.slots[wave];
   auto g0 = [&](uint32_t t) { return g_begin + min(t, nt - 1) * kPrivRows; };
 
   bf16x8_t qb[18];
@@ -203,9 +203,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
 // state goes straight to the workspace: the waves hold different heads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 1) void decode_shared_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) SharedSmem sm;
+  __shared__ __attribute__((aligned(16))) SplitSmem sm;
 
-  const uint32_t n_blk = a.n_groups / 4;
+  const uint32_t n_blk = a.n_groups / kSplitGroups;
   const uint32_t x = blockIdx.x, xcd = x & 7, slot = x >> 3;
   const uint32_t hb = slot % n_blk;
   const uint32_t bs = (slot / n_blk) * 8 + xcd;
@@ -216,40 +216,41 @@ __global__ __launch_bounds__(kThreads, 1) void decode_shared_kernel(DecodeArgs a
   uint32_t r0, r1;
   split_rows(a.seq_base[b + 1] - base, a.n_splits, sp, r0, r1);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hr = lane & 15;
-  const uint32_t g = hb * 4 + wave;
-  const uint32_t head = g * 16 + hr;
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = lane >> 4, hr = lane & 15;
+  const uint32_t g0 = hb * kSplitGroups;  // first head group of the block
 
   bf16x8_t qb[18];
-  load_q(a.q_lat, a.q_rope, b, a.n_heads, head, qb);
-  fill_omega(sm.omega, a.f);
-  f32x4_t o[32];
+  load_q(a.q_lat, a.q_rope, b, a.n_heads, (g0 + w) * 16 + hr, qb);
+  fill_omega(sm.s.omega, a.f);
+  f32x4_t o[kSplitGroups][kSplitNb];
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < kSplitGroups; ++g)
+#pragma unroll
+    for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
   __syncthreads();
 
-  shared_stream(a.ra, sm, base + r0, r1 - r0, [&](const unsigned char* st, uint32_t, uint32_t nrows) {
-    f32x4_t acc[2];
-    qk_blocks<2>(st, st + kTileKr, 0, qb, acc);
-    float sc[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[j][i] = acc[j][i];
-    if (nrows < (uint32_t)kTileRows) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) mask_rows(acc[j], 16 * j, nrows, sc[j]);
-    }
-    float p[2][4];
-    softmax_update_n<2, 32>(sc, a.scale_log2, m, l, o, p);
-    pv_pair<32>(st, 0, 0, pack_p8(p[0], p[1]), o);
+  shared_stream(a.ra, sm.s, base + r0, r1 - r0, [&](const unsigned char* st, uint32_t, uint32_t nrows) {
+    split_tile(sm, st, a.scale_log2, (int32_t)nrows - 1, qb, m, l, o);
   });
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  store_partial(a, ((size_t)b * a.n_splits + sp) * a.n_heads + g * 16, m, l, o);
+  split_publish(sm, m, l);
+  const size_t pbase = ((size_t)b * a.n_splits + sp) * a.n_heads + g0 * 16;
+#pragma unroll
+  for (int g = 0; g < kSplitGroups; ++g) {
+    float* dst = a.ws_acc + (pbase + 16 * g + hr) * IRM_D_LATENT + kSplitCols * w + 4 * hq;
+#pragma unroll
+    for (int nb = 0; nb < kSplitNb; ++nb)
+      *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[g][nb][0], o[g][nb][1], o[g][nb][2], o[g][nb][3]);
+  }
+  if (w == 0 && hq == 0) {
+#pragma unroll
+    for (int g = 0; g < kSplitGroups; ++g) {
+      const float mg = sm.ml[g][hr][0];
+      a.ws_ml[(pbase + 16 * g + hr) * 2 + 0] = mg;
+      a.ws_ml[(pbase + 16 * g + hr) * 2 + 1] = (mg == -INFINITY) ? 0.f : sm.ml[g][hr][1];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -326,9 +327,9 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
   a.n_splits = n_splits;
   a.scale_log2 = scale * kLog2e;
   for (int i = 0; i < (int)kPairs; ++i) a.f.w[i] = t->inv_freq[i];
-  const bool shared = G % 4 == 0;
+  const bool shared = G % kSplitGroups == 0;
   const uint64_t bs = (uint64_t)t->n_seq * n_splits;
-  const uint64_t grid = (bs + 7) / 8 * 8 * (shared ? G / 4 : G);
+  const uint64_t grid = (bs + 7) / 8 * 8 * (shared ? G / kSplitGroups : G);
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");
   if (shared)
     hipLaunchKernelGGL(decode_shared_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);

@@ -20,7 +20,6 @@ constexpr int kUnitsPerRow = kRowBytes / 16;                 // 72
 constexpr int kLatUnits = IRM_D_LATENT * 2 / 16;             // 64
 constexpr int kThreads = 256;                                // 4 waves of 64
 constexpr int kTile = 64;                                    // KV rows per tile
-constexpr int kUnitsPerThread = kTile * kUnitsPerRow / kThreads;  // 18
 constexpr uint32_t kNoRot = 0xffffffffu;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
