@@ -396,48 +396,6 @@ __device__ __forceinline__ void wait_tile(bool d1, bool d2) {
     wait_dma_but<2>();
 }
 
-// Stream assembled rows [g_begin, g_begin + n) and call compute(stage, t,
-// nrows) for every 32-row tile with its k_r rotated.  Every thread of the
-// workgroup calls this with the same arguments; sm.omega must be filled and
-// visible before the call.
-template <class Compute>
-__device__ __forceinline__ void shared_stream(const StreamArgs& ra, SharedSmem& sm, uint32_t g_begin, uint32_t n,
-                                              Compute&& compute) {
-  const uint32_t w = threadIdx.x >> 6;
-  const uint32_t nt = (n + kTileRows - 1) / kTileRows;
-  if (nt == 0) return;
-  WaveSlots<kTileRm, kTileSlice>& ws = sm.slots[w];
-  const uint32_t row0 = kTileSlice * w;
-  int32_t cd[2] = {0, 0};
-  auto g0 = [&](uint32_t x) { return g_begin + min(x, nt - 1) * kTileRows + row0; };
-  auto issue = [&](uint32_t x) {  // data of tile x (if it exists) and row map of tile x+3
-    if (x < nt) slice_issue_data<kTileSlice>(ra, ws.rm[x % kTileRm], sm.stage[x % kStages],
-                                             sm.stage[x % kStages] + kTileKr, row0);
-    slice_issue_rowmap<kTileSlice>(ra, g0(x + 3), ws.rm[(x + 3) % kTileRm]);
-  };
-  auto rotate = [&](uint32_t x) {
-    slice_rotate<kTileSlice>(ws, sm.stage[x % kStages] + kTileKr, row0, sm.omega,
-                             slice_row_delta<kTileSlice>(ws.rm[x % kTileRm]), cd);
-  };
-
-  for (uint32_t x = 0; x < 3; ++x) slice_issue_rowmap<kTileSlice>(ra, g0(x), ws.rm[x]);
-  wait_dma_all();
-  for (uint32_t x = 0; x < 3; ++x) issue(x);
-  wait_tile(1 < nt, 2 < nt);
-  rotate(0);
-  __syncthreads();
-  for (uint32_t t = 0; t < nt; ++t) {
-    issue(t + 3);
-    compute(static_cast<const unsigned char*>(sm.stage[t % kStages]), t, min((uint32_t)kTileRows, n - t * kTileRows));
-    if (t + 1 < nt) {
-      wait_tile(t + 2 < nt, t + 3 < nt);
-      rotate(t + 1);
-    }
-    __syncthreads();
-  }
-  wait_dma_all();
-}
-
 // ---------------------------------------------------------------------------
 // Split tiles: four groups of 16 query-heads per workgroup, output columns
 // split across the waves
@@ -500,68 +458,6 @@ __device__ __forceinline__ bool softmax_scores(const float (&s)[2][4], float c, 
   return moved;
 }
 
-// One 32-row tile.  last is the last visible tile row of the wave's own group
-// (>= 31: the whole tile; < 0: none of it).
-__device__ __forceinline__ void split_tile(SplitSmem& sm, const unsigned char* st, float c, int32_t last,
-                                           const bf16x8_t (&qb)[18], float& m, float& l,
-                                           f32x4_t (&o)[kSplitGroups][kSplitNb]) {
-  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = lane >> 4, hr = lane & 15;
-  // phase A: scores, softmax and P of group w
-  {
-    f32x4_t acc[2];
-    qk_blocks<2>(st, st + kTileKr, 0, qb, acc);
-    float sc[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[j][i] = acc[j][i];
-    if (last < kTileRows - 1) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if ((int32_t)(16 * j + 4 * hq + i) > last) sc[j][i] = -INFINITY;
-    }
-    float p[2][4], alpha;
-    const bool moved = softmax_scores(sc, c, m, l, p, alpha);
-    sm.pfrag[w][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
-    if (hq == 0) sm.alpha[w][hr] = alpha;
-    if (lane == 0) sm.scaled[w] = moved ? 1u : 0u;
-  }
-  __syncthreads();
-  // phase B: O of the four groups over this wave's columns
-  {
-#pragma unroll
-    for (int g = 0; g < kSplitGroups; ++g) {
-      if (sm.scaled[g]) {
-        const float a = sm.alpha[g][hr];
-#pragma unroll
-        for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] *= a;
-      }
-    }
-    bf16x8_t pf[kSplitGroups];
-#pragma unroll
-    for (int g = 0; g < kSplitGroups; ++g) pf[g] = __builtin_bit_cast(bf16x8_t, sm.pfrag[g][lane]);
-    typedef short i16x8_t __attribute__((ext_vector_type(8)));
-    const CtBases c0 = ct_bases(st, 0);
-    auto cread = [&](int nb) {
-      const int n = kSplitNb * w + nb;
-      const i16x4_t lo = ct_read(c0, n);
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4_ptr)(c0.b[n & 7] + 256 * (n >> 3) + 16 * kCkvBytes));
-      return __builtin_bit_cast(bf16x8_t, (i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
-    };
-    bf16x8_t cf[kSplitNb];
-#pragma unroll
-    for (int nb = 0; nb < kSplitNb; ++nb) cf[nb] = cread(nb);
-#pragma unroll
-    for (int nb = 0; nb < kSplitNb; ++nb)
-#pragma unroll
-      for (int g = 0; g < kSplitGroups; ++g)
-        o[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[nb], pf[g], o[g][nb], 0, 0, 0);
-  }
-}
-
 // Owners publish (m, l) of their group; after this every wave can normalise
 // its columns of all four groups.  l is reduced over the lane quarters here.
 __device__ __forceinline__ void split_publish(SplitSmem& sm, float m, float l) {
@@ -573,6 +469,218 @@ __device__ __forceinline__ void split_publish(SplitSmem& sm, float m, float l) {
     sm.ml[w][lane & 15][1] = l;
   }
   __syncthreads();
+}
+
+// The copies of one wave's 8-row slice of a tile, prepared from its row-map
+// records and issued one by one between the score MFMAs of the current tile.
+struct SliceCopies {
+  uint32_t src[kTileSlice];  // pool row of each c_KV row
+  uint32_t ksrc;             // pool row of the k_r row this lane copies
+};
+
+__device__ __forceinline__ SliceCopies prep_copies(const StreamArgs& ra, const uint4* rec) {
+  const uint32_t l = opaque(threadIdx.x & 63);
+  SliceCopies cp;
+#pragma unroll
+  for (int k = 0; k < kTileSlice; ++k) cp.src[k] = min(rec[k].x, ra.pool_last);
+  cp.ksrc = min(rec[l >> 3].x, ra.pool_last);
+  return cp;
+}
+
+// c_KV row row0 + k of the slice into the stage at ckv (1 KB, one copy).
+__device__ __forceinline__ void copy_ckv(const StreamArgs& ra, const SliceCopies& cp, int k, unsigned char* ckv,
+                                         uint32_t row0) {
+  const uint32_t l = threadIdx.x & 63, r = row0 + k;
+  dma16(ra.pool + (size_t)cp.src[k] * kRowBytes + ((l ^ (r & 15)) << 4), lds_addr(ckv + r * kCkvBytes));
+}
+
+// k_r of the slice's 8 rows into the stage's k_r region (1 KB, one copy).
+__device__ __forceinline__ void copy_kr(const StreamArgs& ra, const SliceCopies& cp, unsigned char* kr,
+                                        uint32_t row0) {
+  const uint32_t l = threadIdx.x & 63, r = row0 + (l >> 3);
+  dma16(ra.pool + (size_t)cp.ksrc * kRowBytes + kCkvBytes + (((l & 7) ^ ((r >> 1) & 7)) << 4),
+        lds_addr(kr + row0 * kKrBytes));
+}
+
+// Make the wave's trig table hold the delta of every row of the slice
+// (lane l: row l / 8, delta d).  Returns false if the slice holds more
+// distinct nonzero deltas than the table (two); the caller then rotates with
+// slice_rotate, which handles any number.
+template <int kSlots>
+__device__ __forceinline__ bool slice_trig_ready(WaveSlots<kSlots, kTileSlice>& ws, const double* omega, int32_t d,
+                                                 int32_t (&cd)[2]) {
+  const uint32_t l = threadIdx.x & 63;
+  if (!__any(d != 0 && d != cd[0] && d != cd[1])) return true;
+  const uint64_t nz = __ballot(d != 0);
+  cd[0] = __shfl(d, __ffsll((unsigned long long)nz) - 1);
+  cd[1] = __shfl(d, 63 - __clzll((long long)nz));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  {
+    double sn, cn;
+    sincos((double)cd[l >> 5] * omega[l & 31], &sn, &cn);
+    ws.trig[l >> 5][l & 31] = make_float2((float)cn, (float)sn);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return !__any(d != 0 && d != cd[0] && d != cd[1]);
+}
+
+// Rotate the slice's k_r in place from the table, without branches: lane l
+// turns unit l % 8 of row l / 8; rows with delta 0 go through the identity
+// (cos 1, sin 0), which leaves their bits unchanged.
+template <int kSlots>
+__device__ __forceinline__ void slice_rotate_table(const WaveSlots<kSlots, kTileSlice>& ws, unsigned char* kr,
+                                                   uint32_t row0, int32_t d, const int32_t (&cd)[2]) {
+  const uint32_t l = threadIdx.x & 63, r = row0 + (l >> 3), u = l & 7;
+  const f32x4_t* tp = reinterpret_cast<const f32x4_t*>(&ws.trig[d == cd[0] ? 0 : 1][4 * u]);
+  f32x4_t a = tp[0], b = tp[1];
+  if (d == 0) {
+    a = f32x4_t{1.f, 0.f, 1.f, 0.f};
+    b = a;
+  }
+  u32x4_t* p = reinterpret_cast<u32x4_t*>(kr + kr_pos(r, u));
+  const u32x4_t k = *p;
+  *p = u32x4_t{rotate_pair(k[0], a[0], a[1]), rotate_pair(k[1], a[2], a[3]), rotate_pair(k[2], b[0], b[1]),
+               rotate_pair(k[3], b[2], b[3])};
+}
+
+// Stream assembled rows [g_begin, g_begin + n) through split tiles.
+// Iteration t: phase A scores tile t for the wave's group while the copies of
+// tile t+3 and the row map of tile t+6 go out between its MFMAs; barrier;
+// wait until tile t+1 has landed; phase B accumulates O over the wave's
+// columns while the wave rotates its slice of tile t+1; barrier.  Copies of
+// tiles past the end re-read the last tile into the free stage, so every
+// iteration issues exactly 10 copies per wave and "tile t+1 has landed"
+// is always "at most 20 copies outstanding".  last(t) is the last visible
+// tile row of the wave's group in tile t.  Every thread of the workgroup
+// calls this with the same g_begin, n; sm.s.omega must be visible.
+template <class Last>
+__device__ __forceinline__ void split_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
+                                             float c, Last&& last, const bf16x8_t (&qb)[18], float& m, float& l,
+                                             f32x4_t (&o)[kSplitGroups][kSplitNb]) {
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = lane >> 4, hr = lane & 15;
+  const uint32_t nt = (n + kTileRows - 1) / kTileRows;
+  if (nt == 0) return;
+  WaveSlots<kTileRm, kTileSlice>& ws = sm.s.slots[w];
+  const uint32_t row0 = kTileSlice * w;
+  int32_t cd[2] = {0, 0};
+  auto g0 = [&](uint32_t x) { return g_begin + min(x, nt - 1) * kTileRows + row0; };
+  auto stage = [&](uint32_t x) { return sm.s.stage[x % kStages]; };
+  auto delta = [&](uint32_t x) { return slice_row_delta<kTileSlice>(ws.rm[x % kTileRm]); };
+  auto issue_all = [&](uint32_t x) {  // copies of tile x and the row map of tile x+3
+    const SliceCopies cp = prep_copies(ra, ws.rm[x % kTileRm]);
+#pragma unroll
+    for (int k = 0; k < kTileSlice; ++k) copy_ckv(ra, cp, k, stage(x), row0);
+    copy_kr(ra, cp, stage(x) + kTileKr, row0);
+    slice_issue_rowmap<kTileSlice>(ra, g0(x + 3), ws.rm[(x + 3) % kTileRm]);
+  };
+
+  for (uint32_t x = 0; x < 3; ++x) slice_issue_rowmap<kTileSlice>(ra, g0(x), ws.rm[x]);
+  wait_dma_all();
+  for (uint32_t x = 0; x < 3; ++x) issue_all(x);
+  wait_dma_but<20>();
+  slice_rotate<kTileSlice>(ws, stage(0) + kTileKr, row0, sm.s.omega, delta(0), cd);
+  __syncthreads();
+
+  for (uint32_t t = 0; t < nt; ++t) {
+    const unsigned char* st = stage(t);
+    unsigned char* nx = stage(t + 3);
+    // phase A: scores of group w, copies of tile t+3 in between
+    {
+      const SliceCopies cp = prep_copies(ra, ws.rm[(t + 3) % kTileRm]);
+      const uint32_t ln = opaque(lane), q = ln >> 4, rr = ln & 15;
+      const unsigned char* rowp = st + rr * kCkvBytes + ((q ^ (rr & 3)) << 4);
+      const unsigned char* base[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[i] = rowp + (((uint32_t)i ^ (rr >> 2)) << 6);
+      const unsigned char* krp[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) krp[i] = st + kTileKr + kr_pos(rr, 4 * i + q);
+      auto read = [&](int kk, bf16x8_t (&a)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const unsigned char* ptr = kk < 16 ? base[kk & 3] + 256 * (kk >> 2) + 16 * j * kCkvBytes
+                                             : krp[kk - 16] + 16 * j * kKrBytes;
+          a[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ptr));
+        }
+      };
+      f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      bf16x8_t cur[2], nxt[2];
+      read(0, cur);
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+        if (kk + 1 < 18) read(kk + 1, nxt);
+        if ((kk & 1) == 0 && kk < 2 * kTileSlice) copy_ckv(ra, cp, kk >> 1, nx, row0);
+        if (kk == 2 * kTileSlice) copy_kr(ra, cp, nx + kTileKr, row0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[j], qb[kk], acc[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) cur[j] = nxt[j];
+      }
+      slice_issue_rowmap<kTileSlice>(ra, g0(t + 6), ws.rm[(t + 6) % kTileRm]);
+      float sc[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[j][i] = acc[j][i];
+      const int32_t lv = last(t, min((uint32_t)kTileRows, n - t * kTileRows));
+      if (lv < kTileRows - 1) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((int32_t)(16 * j + 4 * hq + i) > lv) sc[j][i] = -INFINITY;
+      }
+      float p[2][4], alpha;
+      const bool moved = softmax_scores(sc, c, m, l, p, alpha);
+      sm.pfrag[w][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
+      if (hq == 0) sm.alpha[w][hr] = alpha;
+      if (lane == 0) sm.scaled[w] = moved ? 1u : 0u;
+    }
+    __syncthreads();
+    wait_dma_but<20>();  // tile t+1 (or its stand-in past the end) has landed
+    // rare: a new delta in the next slice, or a moved reference maximum
+    const int32_t dn = delta(t + 1);
+    const bool table_ok = slice_trig_ready(ws, sm.s.omega, dn, cd);
+    if (!table_ok) slice_rotate<kTileSlice>(ws, stage(t + 1) + kTileKr, row0, sm.s.omega, dn, cd);
+    if (sm.scaled[0] | sm.scaled[1] | sm.scaled[2] | sm.scaled[3]) {
+#pragma unroll
+      for (int g = 0; g < kSplitGroups; ++g) {
+        const float a = sm.alpha[g][hr];
+#pragma unroll
+        for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] *= a;
+      }
+    }
+    // phase B: O of the four groups over this wave's columns, rotation of
+    // the wave's slice of tile t+1 in between
+    {
+      bf16x8_t pf[kSplitGroups];
+#pragma unroll
+      for (int g = 0; g < kSplitGroups; ++g) pf[g] = __builtin_bit_cast(bf16x8_t, sm.pfrag[g][lane]);
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const CtBases c0 = ct_bases(st, 0);
+      bf16x8_t cf[kSplitNb];
+#pragma unroll
+      for (int nb = 0; nb < kSplitNb; ++nb) {
+        const int nn = kSplitNb * w + nb;
+        const i16x4_t lo = ct_read(c0, nn);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_ptr)(c0.b[nn & 7] + 256 * (nn >> 3) + 16 * kCkvBytes));
+        cf[nb] = __builtin_bit_cast(bf16x8_t, (i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
+      }
+      // identity when slice_rotate already turned the slice (bits unchanged)
+      slice_rotate_table(ws, stage(t + 1) + kTileKr, row0, table_ok ? dn : 0, cd);
+#pragma unroll
+      for (int nb = 0; nb < kSplitNb; ++nb)
+#pragma unroll
+        for (int g = 0; g < kSplitGroups; ++g)
+          o[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[nb], pf[g], o[g][nb], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  wait_dma_all();
 }
 
 }  // namespace dev

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
 // Workgroup = (sequence, split, 64-head block); wave w owns head group
 // 4 blk + w.  All four waves read every tile of the split, so the KV
 // is copied once per 64 heads instead of once per 16; each wave copies and
-// rotates one 8-row slice of every 32-row tile (shared_stream).  A wave's partial
+// rotates one 8-row slice of every 32-row tile (split_stream).  A wave's partial
 // state goes straight to the workspace: the waves hold different heads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 1) void decode_shared_kernel(DecodeArgs a) {
@@ -230,9 +230,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_shared_kernel(DecodeArgs a
   float m = -INFINITY, l = 0.f;
   __syncthreads();
 
-  shared_stream(a.ra, sm.s, base + r0, r1 - r0, [&](const unsigned char* st, uint32_t, uint32_t nrows) {
-    split_tile(sm, st, a.scale_log2, (int32_t)nrows - 1, qb, m, l, o);
-  });
+  split_stream(a.ra, sm, base + r0, r1 - r0, a.scale_log2,
+               [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l, o);
 
   split_publish(sm, m, l);
   const size_t pbase = ((size_t)b * a.n_splits + sp) * a.n_heads + g0 * 16;

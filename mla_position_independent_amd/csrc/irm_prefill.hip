@@ -16,7 +16,7 @@ using namespace irm::dev;
 // ---------------------------------------------------------------------------
 // Four queries per workgroup, one 16-head group: the four (query, 16 heads)
 // groups share every 32-row tile of the causal range of the last query
-// (shared_stream copies, split_tile computes).  Wave w scores query w and
+// (split_stream).  Wave w scores query w and
 // accumulates output columns 128 w .. 128 w + 127 of all four.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kQueriesPerBlock = kSplitGroups;
@@ -57,10 +57,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY, l = 0.f;
   __syncthreads();
 
-  shared_stream(a.ra, sm.s, a.seq_base[0], rows, [&](const unsigned char* st, uint32_t t, uint32_t) {
-    const int64_t last = lim - (int64_t)t * kTileRows;
-    split_tile(sm, st, a.scale_log2, last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last), qb, m, l, o);
-  });
+  split_stream(a.ra, sm, a.seq_base[0], rows, a.scale_log2,
+               [&](uint32_t t, uint32_t) -> int32_t {
+                 const int64_t last = lim - (int64_t)t * kTileRows;
+                 return last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last);
+               },
+               qb, m, l, o);
 
   split_publish(sm, m, l);
 #pragma unroll
