@@ -36,7 +36,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources that define each timed kernel (a counter record is valid only for these bytes)
 KERNEL_SOURCES = {
     "rotate_gather_kernel": ["irm_gather.hip", "irm_device.h"],
-    "decode_split_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
+    "decode_private_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
+    "decode_shared_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
     "prefill_kernel": ["irm_prefill.hip", "irm_attn.h", "irm_device.h"],
 }
 
@@ -191,6 +192,9 @@ def leg_decode(args, irm, torch, synth, name, make):
             ev[1].record()
 
     ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    # the split pass runs one 16-head group per workgroup unless the head
+    # count is a multiple of 64 (four groups share every KV tile)
+    kernel = "decode_shared_kernel" if H % 64 == 0 else "decode_private_kernel"
     kv = ROW_BYTES * t.total_rows
     qo = w.n_seq * H * (576 + 512) * 2
     alg_bytes = kv + qo
@@ -201,8 +205,8 @@ def leg_decode(args, irm, torch, synth, name, make):
         "workload": w.name, "ms_per_call": round(kern_ms, 4), "tokens": t.total_rows, "n_splits": w.n_splits,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("decode_split_kernel:" + w.name),
-                     "kernel": "decode_split_kernel + decode_combine_kernel",
+                     "traffic": measured_traffic(kernel + ":" + w.name),
+                     "kernel": kernel + " + decode_combine_kernel",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
     }
@@ -279,7 +283,8 @@ def main():
                     help="run the named legs only, without the JSON line or the CPU baseline")
     ap.add_argument("--ingest-counters", nargs=5, metavar=("KEY", "FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="record rocprofv3 FETCH_SIZE/WRITE_SIZE runs of a kernel (scaled by the copy runs) "
-                         "in profiles/traffic.json and exit; KEY is e.g. rotate_gather_kernel")
+                         "in profiles/traffic.json and exit; KEY is e.g. rotate_gather_kernel or "
+                         "decode_private_kernel:<workload name>")
     args = ap.parse_args()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters)
