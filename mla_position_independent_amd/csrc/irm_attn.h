@@ -5,6 +5,8 @@
 // score = q_lat . c_KV + q_rope . k_r over the 576-wide row, value = c_KV.
 #pragma once
 
+#include <type_traits>
+
 #include "irm_device.h"
 
 namespace irm {
@@ -362,15 +364,8 @@ __device__ __forceinline__ void wait_dma_but() { asm volatile("s_waitcnt vmcnt(%
 // ---------------------------------------------------------------------------
 // Shared 32-row tiles: four waves each copy and rotate one 8-row slice of
 // every tile into a four-stage LDS ring, and all four compute on the whole
-// tile.
-//
-// Iteration t: issue the data of tile t+3 into the stage tile t-1 left free
-// and the row map of tile t+6, compute tile t, wait until tile t+1 has
-// landed, rotate this wave's slice of tile t+1, barrier.  One barrier per
-// tile publishes tile t+1 and frees tile t's stage.  Copies per iteration
-// and wave: 9 data (only while tile t+3 exists) + 1 row map (always; past the
-// end it re-reads the last tile's records), so the wait for tile t+1 lets the
-// copies of iterations t-1 and t stay outstanding: 20, 11 or 2 of them.
+// tile.  A stage holds the tile's c_KV rows (1 KB each, 16-byte units
+// swizzled by row) and then its k_r rows (128 B each).
 // ---------------------------------------------------------------------------
 constexpr int kTileRows = 32;
 constexpr int kStages = 4;
@@ -385,31 +380,20 @@ struct SharedSmem {
   double omega[kPairs];
 };
 
-// Wait until the data of tile x has landed, given which of tiles x+1, x+2
-// were issued after it (d1 implies d0's tile exists too).
-__device__ __forceinline__ void wait_tile(bool d1, bool d2) {
-  if (d2)
-    wait_dma_but<20>();
-  else if (d1)
-    wait_dma_but<11>();
-  else
-    wait_dma_but<2>();
-}
-
 // ---------------------------------------------------------------------------
 // Split tiles: four groups of 16 query-heads per workgroup, output columns
-// split across the waves
+// split across the accumulating waves
 //
 // Each 32-row tile serves four groups of 16 query-heads (four queries of one
-// head group in prefill, four head groups of one query in decode).  Wave w
-// scores group w (K fragments from LDS, Q in registers), runs its online
-// softmax, and publishes the probabilities (already in the lane layout of
-// the PV B operand) and any rescale factors through LDS.  After a barrier,
-// wave w accumulates O for all four groups over output columns
-// 128 w .. 128 w + 127, so every C^T fragment it reads feeds four MFMAs.
-// Per tile and wave: 36 + 32 MFMAs; LDS reads 36 KB (K) + 8 KB (C^T) + 4 KB
-// (P), against 36 KB + 32 KB when every wave accumulates all columns of its
-// own group.
+// head group in prefill, four head groups of one query in decode).  Scoring
+// wave s computes the scores of group s (K fragments from LDS, Q in
+// registers), runs its online softmax, and publishes the probabilities
+// (already in the lane layout of the PV B operand) and any rescale factors
+// through LDS.  After a barrier, accumulating wave j sums O for all four
+// groups over output columns 128 j .. 128 j + 127, so every C^T fragment it
+// reads feeds four MFMAs.  Per tile and SIMD: 36 + 32 MFMAs; LDS reads 36 KB
+// (K) + 8 KB (C^T) + 4 KB (P), against 36 KB + 32 KB when one wave
+// accumulates all columns of its own group.
 // ---------------------------------------------------------------------------
 constexpr int kSplitGroups = 4;
 constexpr int kSplitCols = IRM_D_LATENT / kSplitGroups;  // 128 output columns per wave
@@ -417,16 +401,28 @@ constexpr int kSplitNb = kSplitCols / 16;                // 8 column blocks
 
 struct SplitSmem {
   SharedSmem s;
-  uint4 pfrag[kSplitGroups][64];  // P^T operand of group g for lane l (8 bf16)
-  float alpha[kSplitGroups][16];  // rescale factor of group g, head l % 16
-  uint32_t scaled[kSplitGroups];  // group g moved its reference maximum on this tile
-  float ml[kSplitGroups][16][2];  // final (m, l) of group g, head l % 16
+  // per tile parity: P of tile t is produced in iteration t and consumed in t+1
+  uint4 pfrag[2][kSplitGroups][64];  // P^T operand of group g for lane l (8 bf16)
+  float alpha[2][kSplitGroups][16];  // rescale factor of group g, head l % 16
+  uint32_t scaled[2][kSplitGroups];  // group g moved its reference maximum on that tile
+  float ml[kSplitGroups][16][2];     // final (m, l) of group g, head l % 16
 };
 static_assert(sizeof(SplitSmem) <= 160 * 1024, "split tiles fit the LDS");
 
+// Maximum over the four lane quarters of a wave (lanes l, l^16, l^32, l^48),
+// with the two permlane swaps: each gives every lane its own value and its
+// partner's, in some order.
+__device__ __forceinline__ float max_quarters(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Online softmax of one group over 2 blocks of 4 raw scores per lane (-inf
-// where masked), without touching O: leaves p, returns alpha (1 if the
-// reference maximum did not move) and whether any head moved it.
+// where masked), without touching O and without branches: leaves p and
+// alpha (1 where the head's reference maximum did not move), returns whether
+// any head moved it.
 __device__ __forceinline__ bool softmax_scores(const float (&s)[2][4], float c, float& m, float& l,
                                                float (&p)[2][4], float& alpha) {
   float mx = -INFINITY;
@@ -434,17 +430,13 @@ __device__ __forceinline__ bool softmax_scores(const float (&s)[2][4], float c, 
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_quarters(mx);
   const float mxc = mx * c;
-  alpha = 1.f;
-  const bool moved = __any(mxc > m + kSlack);
-  if (moved) {
-    const float m_new = (mxc > m + kSlack) ? mxc : m;
-    alpha = __builtin_amdgcn_exp2f(m - m_new);
-    l *= alpha;
-    m = m_new;
-  }
+  const bool mv = mxc > m + kSlack;
+  const float m_new = mv ? mxc : m;
+  alpha = mv ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+  l *= alpha;
+  m = m_new;
   const float m_use = (m == -INFINITY) ? 0.f : m;
   float sum = 0.f;
 #pragma unroll
@@ -455,11 +447,13 @@ __device__ __forceinline__ bool softmax_scores(const float (&s)[2][4], float c, 
       sum += p[j][i];
     }
   l += sum;
-  return moved;
+  return __any(mv);
 }
 
-// Owners publish (m, l) of their group; after this every wave can normalise
-// its columns of all four groups.  l is reduced over the lane quarters here.
+// Scoring waves publish (m, l) of their group; after this every
+// accumulating wave can normalise its columns of all four groups.  l is
+// reduced over the lane quarters here.  The accumulating waves meet the
+// barrier with split_publish_wait.
 __device__ __forceinline__ void split_publish(SplitSmem& sm, float m, float l) {
   const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   l += __shfl_xor(l, 16);
@@ -470,6 +464,8 @@ __device__ __forceinline__ void split_publish(SplitSmem& sm, float m, float l) {
   }
   __syncthreads();
 }
+
+__device__ __forceinline__ void split_publish_wait() { __syncthreads(); }
 
 // The copies of one wave's 8-row slice of a tile, prepared from its row-map
 // records and issued one by one between the score MFMAs of the current tile.
@@ -527,159 +523,212 @@ __device__ __forceinline__ bool slice_trig_ready(WaveSlots<kSlots, kTileSlice>& 
   return !__any(d != 0 && d != cd[0] && d != cd[1]);
 }
 
-// Rotate the slice's k_r in place from the table, without branches: lane l
-// turns unit l % 8 of row l / 8; rows with delta 0 go through the identity
-// (cos 1, sin 0), which leaves their bits unchanged.
+// Rotation of the slice's k_r from the table in two halves, so that the
+// LDS read can be issued well before the arithmetic and the write: lane l
+// turns unit l % 8 of row l / 8; rows with delta 0 take the identity (cos 1,
+// sin 0).
+struct SliceRot {
+  u32x4_t k;
+  f32x4_t a, b;
+};
+
 template <int kSlots>
-__device__ __forceinline__ void slice_rotate_table(const WaveSlots<kSlots, kTileSlice>& ws, unsigned char* kr,
+__device__ __forceinline__ SliceRot slice_rot_load(const WaveSlots<kSlots, kTileSlice>& ws, const unsigned char* kr,
                                                    uint32_t row0, int32_t d, const int32_t (&cd)[2]) {
   const uint32_t l = threadIdx.x & 63, r = row0 + (l >> 3), u = l & 7;
   const f32x4_t* tp = reinterpret_cast<const f32x4_t*>(&ws.trig[d == cd[0] ? 0 : 1][4 * u]);
-  f32x4_t a = tp[0], b = tp[1];
+  SliceRot x;
+  x.a = tp[0];
+  x.b = tp[1];
   if (d == 0) {
-    a = f32x4_t{1.f, 0.f, 1.f, 0.f};
-    b = a;
+    x.a = f32x4_t{1.f, 0.f, 1.f, 0.f};
+    x.b = x.a;
   }
-  u32x4_t* p = reinterpret_cast<u32x4_t*>(kr + kr_pos(r, u));
-  const u32x4_t k = *p;
-  *p = u32x4_t{rotate_pair(k[0], a[0], a[1]), rotate_pair(k[1], a[2], a[3]), rotate_pair(k[2], b[0], b[1]),
-               rotate_pair(k[3], b[2], b[3])};
+  x.k = *reinterpret_cast<const u32x4_t*>(kr + kr_pos(r, u));
+  return x;
 }
 
-// Stream assembled rows [g_begin, g_begin + n) through split tiles.
-// Iteration t: phase A scores tile t for the wave's group while the copies of
-// tile t+3 and the row map of tile t+6 go out between its MFMAs; barrier;
-// wait until tile t+1 has landed; phase B accumulates O over the wave's
-// columns while the wave rotates its slice of tile t+1; barrier.  Copies of
-// tiles past the end re-read the last tile into the free stage, so every
-// iteration issues exactly 10 copies per wave and "tile t+1 has landed"
-// is always "at most 20 copies outstanding".  last(t) is the last visible
-// tile row of the wave's group in tile t.  Every thread of the workgroup
-// calls this with the same g_begin, n; sm.s.omega must be visible.
+__device__ __forceinline__ void slice_rot_store(unsigned char* kr, uint32_t row0, const SliceRot& x) {
+  const uint32_t l = threadIdx.x & 63, r = row0 + (l >> 3), u = l & 7;
+  *reinterpret_cast<u32x4_t*>(kr + kr_pos(r, u)) =
+      u32x4_t{rotate_pair(x.k[0], x.a[0], x.a[1]), rotate_pair(x.k[1], x.a[2], x.a[3]),
+              rotate_pair(x.k[2], x.b[0], x.b[1]), rotate_pair(x.k[3], x.b[2], x.b[3])};
+}
+
+// ---------------------------------------------------------------------------
+// Role-split streaming of split tiles: eight waves per workgroup, two per
+// SIMD.  Waves 0..3 score: wave s holds Q of group s, computes S^T of every
+// tile, runs the online softmax and publishes P and the rescale factors.
+// Waves 4..7 accumulate: wave 4+j copies and rotates slice j (rows 8j..8j+7)
+// of every tile and accumulates O of all four groups over output columns
+// 128 j .. 128 j + 127.  Each SIMD thus runs one wave of each kind, and
+// either covers the other's LDS, copy and barrier waits with its MFMAs.
+//
+// Iteration t (0 <= t <= nt) ends with one barrier.  Scorers: tile t (t < nt)
+// -> P under parity t.  Accumulators: PV of tile t-1 (t >= 1) from the P
+// published one iteration earlier, interleaved with the copies of tile t+2;
+// the row map of tile t+4; wait for tile t+1 and rotate their slice of it.
+// Stages in use during iteration t: t-1 (PV), t (QK), t+1 (rotate), t+2
+// (copies in flight).  Copies of tiles past the end re-read the last tile
+// into the free stage, so every iteration issues kTileCopies copies per
+// accumulator and "tile t+1 has landed" is "at most kTileCopies outstanding"
+// (the copies of tile t+2 and the row map of tile t+4).  Barriers per call:
+// nt + 2 on both sides, none when nt = 0.
+// ---------------------------------------------------------------------------
+constexpr int kRoleThreads = 2 * kThreads;
+constexpr int kTileCopies = kTileSlice + 1 + 1;  // c_KV rows, k_r, row map
+
+// Wave index as a scalar: roles branch on it without divergence.
+__device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Scorer side.  last(t, nrows) is the last visible tile row of the wave's
+// group in tile t (nrows rows of the tile exist).
 template <class Last>
-__device__ __forceinline__ void split_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
-                                             float c, Last&& last, const bf16x8_t (&qb)[18], float& m, float& l,
-                                             f32x4_t (&o)[kSplitGroups][kSplitNb]) {
-  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = lane >> 4, hr = lane & 15;
+__device__ __forceinline__ void score_stream(SplitSmem& sm, uint32_t n, float c, Last&& last,
+                                             const bf16x8_t (&qb)[18], float& m, float& l) {
+  const uint32_t lane = threadIdx.x & 63, s = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
-  WaveSlots<kTileRm, kTileSlice>& ws = sm.s.slots[w];
-  const uint32_t row0 = kTileSlice * w;
+  __syncthreads();  // tile 0 is in place
+  const uint32_t ln = opaque(lane), q = ln >> 4, rr = ln & 15;
+  for (uint32_t t = 0; t < nt; ++t) {
+    const unsigned char* sa = sm.s.stage[t % kStages];
+    const unsigned char* rowp = sa + rr * kCkvBytes + ((q ^ (rr & 3)) << 4);
+    const unsigned char* base[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) base[i] = rowp + (((uint32_t)i ^ (rr >> 2)) << 6);
+    const unsigned char* krp[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) krp[i] = sa + kTileKr + kr_pos(rr, 4 * i + q);
+    auto read = [&](int kk, bf16x8_t (&x)[2]) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const unsigned char* ptr = kk < 16 ? base[kk & 3] + 256 * (kk >> 2) + 16 * j * kCkvBytes
+                                           : krp[kk - 16] + 16 * j * kKrBytes;
+        x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ptr));
+      }
+    };
+    constexpr int kAhead = 8;
+    bf16x8_t ring[kAhead + 1][2];
+#pragma unroll
+    for (int kk = 0; kk < kAhead; ++kk) read(kk, ring[kk]);
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      if (kk + kAhead < 18) read(kk + kAhead, ring[(kk + kAhead) % (kAhead + 1)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[kk % (kAhead + 1)][j], qb[kk], acc[j], 0, 0, 0);
+    }
+    const int32_t lv = last(t, min((uint32_t)kTileRows, n - t * kTileRows));
+    float sc[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[j][i] = ((int32_t)(16 * j + 4 * hq + i) > lv) ? -INFINITY : acc[j][i];
+    float p[2][4], alpha;
+    const bool moved = softmax_scores(sc, c, m, l, p, alpha);
+    sm.pfrag[t & 1][s][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
+    if (hq == 0) sm.alpha[t & 1][s][hr] = alpha;
+    if (lane == 0) sm.scaled[t & 1][s] = moved ? 1u : 0u;
+    __syncthreads();
+  }
+  __syncthreads();  // the accumulators' last PV
+}
+
+// Accumulator side: rows [g_begin, g_begin + n) of the assembled sequence.
+// sm.s.omega must be visible.  The row-map data an iteration needs (copy
+// sources of tile t+2, deltas of tile t+1) is read into registers one
+// iteration ahead, so that the only LDS round trips on the way from one
+// barrier to the next are the P / C^T fragments and the k_r to rotate.
+__device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
+                                             f32x4_t (&o)[kSplitGroups][kSplitNb]) {
+  static_assert(kTileCopies == 10, "the waits below count 10 copies per iteration");
+  const uint32_t lane = threadIdx.x & 63, j = wave_id() - kSplitGroups, hr = lane & 15;
+  const uint32_t nt = (n + kTileRows - 1) / kTileRows;
+  if (nt == 0) return;
+  WaveSlots<kTileRm, kTileSlice>& ws = sm.s.slots[j];
+  const uint32_t row0 = kTileSlice * j;
   int32_t cd[2] = {0, 0};
   auto g0 = [&](uint32_t x) { return g_begin + min(x, nt - 1) * kTileRows + row0; };
   auto stage = [&](uint32_t x) { return sm.s.stage[x % kStages]; };
   auto delta = [&](uint32_t x) { return slice_row_delta<kTileSlice>(ws.rm[x % kTileRm]); };
-  auto issue_all = [&](uint32_t x) {  // copies of tile x and the row map of tile x+3
-    const SliceCopies cp = prep_copies(ra, ws.rm[x % kTileRm]);
-#pragma unroll
-    for (int k = 0; k < kTileSlice; ++k) copy_ckv(ra, cp, k, stage(x), row0);
-    copy_kr(ra, cp, stage(x) + kTileKr, row0);
-    slice_issue_rowmap<kTileSlice>(ra, g0(x + 3), ws.rm[(x + 3) % kTileRm]);
-  };
 
-  for (uint32_t x = 0; x < 3; ++x) slice_issue_rowmap<kTileSlice>(ra, g0(x), ws.rm[x]);
-  wait_dma_all();
-  for (uint32_t x = 0; x < 3; ++x) issue_all(x);
-  wait_dma_but<20>();
-  slice_rotate<kTileSlice>(ws, stage(0) + kTileKr, row0, sm.s.omega, delta(0), cd);
-  __syncthreads();
+  SliceCopies cp;  // copy sources of tile t+2
+  int32_t d1;      // delta of this lane's row of tile t+1
 
-  for (uint32_t t = 0; t < nt; ++t) {
-    const unsigned char* st = stage(t);
-    unsigned char* nx = stage(t + 3);
-    // phase A: scores of group w, copies of tile t+3 in between
-    {
-      const SliceCopies cp = prep_copies(ra, ws.rm[(t + 3) % kTileRm]);
-      const uint32_t ln = opaque(lane), q = ln >> 4, rr = ln & 15;
-      const unsigned char* rowp = st + rr * kCkvBytes + ((q ^ (rr & 3)) << 4);
-      const unsigned char* base[4];
+  // kB: tile t-1 exists (t >= 1)
+  auto iteration = [&](uint32_t t, auto kB) {
+    constexpr bool B = decltype(kB)::value;
+    unsigned char* nx = stage(t + 2);
+    if constexpr (B) {
+      const uint32_t pb = (t - 1) & 1;
+      const uint4 scaled = *reinterpret_cast<const uint4*>(sm.scaled[pb]);
+      bf16x8_t pf[kSplitGroups], cf[kSplitNb];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) base[i] = rowp + (((uint32_t)i ^ (rr >> 2)) << 6);
-      const unsigned char* krp[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) krp[i] = st + kTileKr + kr_pos(rr, 4 * i + q);
-      auto read = [&](int kk, bf16x8_t (&a)[2]) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const unsigned char* ptr = kk < 16 ? base[kk & 3] + 256 * (kk >> 2) + 16 * j * kCkvBytes
-                                             : krp[kk - 16] + 16 * j * kKrBytes;
-          a[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ptr));
-        }
-      };
-      f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-      bf16x8_t cur[2], nxt[2];
-      read(0, cur);
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        if (kk + 1 < 18) read(kk + 1, nxt);
-        if ((kk & 1) == 0 && kk < 2 * kTileSlice) copy_ckv(ra, cp, kk >> 1, nx, row0);
-        if (kk == 2 * kTileSlice) copy_kr(ra, cp, nx + kTileKr, row0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur[j], qb[kk], acc[j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) cur[j] = nxt[j];
-      }
-      slice_issue_rowmap<kTileSlice>(ra, g0(t + 6), ws.rm[(t + 6) % kTileRm]);
-      float sc[2][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[j][i] = acc[j][i];
-      const int32_t lv = last(t, min((uint32_t)kTileRows, n - t * kTileRows));
-      if (lv < kTileRows - 1) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((int32_t)(16 * j + 4 * hq + i) > lv) sc[j][i] = -INFINITY;
-      }
-      float p[2][4], alpha;
-      const bool moved = softmax_scores(sc, c, m, l, p, alpha);
-      sm.pfrag[w][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
-      if (hq == 0) sm.alpha[w][hr] = alpha;
-      if (lane == 0) sm.scaled[w] = moved ? 1u : 0u;
-    }
-    __syncthreads();
-    wait_dma_but<20>();  // tile t+1 (or its stand-in past the end) has landed
-    // rare: a new delta in the next slice, or a moved reference maximum
-    const int32_t dn = delta(t + 1);
-    const bool table_ok = slice_trig_ready(ws, sm.s.omega, dn, cd);
-    if (!table_ok) slice_rotate<kTileSlice>(ws, stage(t + 1) + kTileKr, row0, sm.s.omega, dn, cd);
-    if (sm.scaled[0] | sm.scaled[1] | sm.scaled[2] | sm.scaled[3]) {
-#pragma unroll
-      for (int g = 0; g < kSplitGroups; ++g) {
-        const float a = sm.alpha[g][hr];
-#pragma unroll
-        for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] *= a;
-      }
-    }
-    // phase B: O of the four groups over this wave's columns, rotation of
-    // the wave's slice of tile t+1 in between
-    {
-      bf16x8_t pf[kSplitGroups];
-#pragma unroll
-      for (int g = 0; g < kSplitGroups; ++g) pf[g] = __builtin_bit_cast(bf16x8_t, sm.pfrag[g][lane]);
+      for (int g = 0; g < kSplitGroups; ++g) pf[g] = __builtin_bit_cast(bf16x8_t, sm.pfrag[pb][g][lane]);
       typedef short i16x8_t __attribute__((ext_vector_type(8)));
-      const CtBases c0 = ct_bases(st, 0);
-      bf16x8_t cf[kSplitNb];
+      const CtBases c0 = ct_bases(stage(t - 1), 0);
 #pragma unroll
       for (int nb = 0; nb < kSplitNb; ++nb) {
-        const int nn = kSplitNb * w + nb;
+        const int nn = kSplitNb * j + nb;
         const i16x4_t lo = ct_read(c0, nn);
         const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4_ptr)(c0.b[nn & 7] + 256 * (nn >> 3) + 16 * kCkvBytes));
         cf[nb] = __builtin_bit_cast(bf16x8_t, (i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
       }
-      // identity when slice_rotate already turned the slice (bits unchanged)
-      slice_rotate_table(ws, stage(t + 1) + kTileKr, row0, table_ok ? dn : 0, cd);
+      if (scaled.x | scaled.y | scaled.z | scaled.w) {
 #pragma unroll
-      for (int nb = 0; nb < kSplitNb; ++nb)
+        for (int g = 0; g < kSplitGroups; ++g) {
+          const float a = sm.alpha[pb][g][hr];
+#pragma unroll
+          for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] *= a;
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < kSplitNb; ++nb) {
+        copy_ckv(ra, cp, nb, nx, row0);
 #pragma unroll
         for (int g = 0; g < kSplitGroups; ++g)
           o[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[nb], pf[g], o[g][nb], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kTileSlice; ++k) copy_ckv(ra, cp, k, nx, row0);
+    }
+    copy_kr(ra, cp, nx + kTileKr, row0);
+    slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);
+    const bool rot = t + 1 < nt;
+    const bool table = rot && slice_trig_ready(ws, sm.s.omega, d1, cd);
+    wait_dma_but<kTileCopies>();  // tile t+1 and the row map of tile t+3 have landed
+    const int32_t d_rot = d1;
+    cp = prep_copies(ra, ws.rm[(t + 3) % kTileRm]);
+    d1 = delta(t + 2);
+    if (rot) {
+      unsigned char* sr = stage(t + 1) + kTileKr;
+      if (table)
+        slice_rot_store(sr, row0, slice_rot_load(ws, sr, row0, d_rot, cd));
+      else
+        slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d_rot, cd);
     }
     __syncthreads();
+  };
+
+  for (uint32_t x = 0; x < 4; ++x) slice_issue_rowmap<kTileSlice>(ra, g0(x), ws.rm[x]);
+  wait_dma_all();
+  for (uint32_t x = 0; x < 2; ++x) {  // copies of tiles 0 and 1 (iterations 0, 1 fetch row maps 4, 5)
+    const SliceCopies c = prep_copies(ra, ws.rm[x]);
+#pragma unroll
+    for (int k = 0; k < kTileSlice; ++k) copy_ckv(ra, c, k, stage(x), row0);
+    copy_kr(ra, c, stage(x) + kTileKr, row0);
   }
+  cp = prep_copies(ra, ws.rm[2]);
+  d1 = delta(1);
+  wait_dma_but<kTileCopies - 1>();  // tile 0 has landed (tile 1's copies may be outstanding)
+  slice_rotate<kTileSlice>(ws, stage(0) + kTileKr, row0, sm.s.omega, delta(0), cd);
+  __syncthreads();
+  iteration(0, std::false_type{});
+  for (uint32_t t = 1; t <= nt; ++t) iteration(t, std::true_type{});
   wait_dma_all();
 }
 

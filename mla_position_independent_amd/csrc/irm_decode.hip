@@ -196,13 +196,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
 // ---------------------------------------------------------------------------
 // split-KV decode, pass 1, four 16-head groups per workgroup: shared tiles
 //
-// Workgroup = (sequence, split, 64-head block); wave w owns head group
-// 4 blk + w.  All four waves read every tile of the split, so the KV
-// is copied once per 64 heads instead of once per 16; each wave copies and
-// rotates one 8-row slice of every 32-row tile (split_stream).  A wave's partial
-// state goes straight to the workspace: the waves hold different heads.
+// Workgroup = (sequence, split, 64-head block) of eight waves.  Scoring
+// wave s holds head group 4 blk + s; accumulating wave j copies and rotates
+// one 8-row slice of every 32-row tile and sums columns 128 j .. 128 j + 127
+// of all four groups (score_stream / value_stream), so the KV is copied once
+// per 64 heads instead of once per 16.  Partial states go straight to the
+// workspace: O from the accumulating waves, (m, l) from the scoring waves.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 1) void decode_shared_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) SplitSmem sm;
 
   const uint32_t n_blk = a.n_groups / kSplitGroups;
@@ -216,39 +217,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_shared_kernel(DecodeArgs a
   uint32_t r0, r1;
   split_rows(a.seq_base[b + 1] - base, a.n_splits, sp, r0, r1);
 
-  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = lane >> 4, hr = lane & 15;
+  const uint32_t lane = threadIdx.x & 63, w = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t g0 = hb * kSplitGroups;  // first head group of the block
-
-  bf16x8_t qb[18];
-  load_q(a.q_lat, a.q_rope, b, a.n_heads, (g0 + w) * 16 + hr, qb);
+  const size_t pbase = ((size_t)b * a.n_splits + sp) * a.n_heads + g0 * 16;
   fill_omega(sm.s.omega, a.f);
+
+  if (w < kSplitGroups) {  // scoring wave: head group g0 + w
+    bf16x8_t qb[18];
+    load_q<false>(a.q_lat, a.q_rope, b, a.n_heads, (g0 + w) * 16 + hr, qb);
+    float m = -INFINITY, l = 0.f;
+    __syncthreads();
+    score_stream(sm, r1 - r0, a.scale_log2,
+                 [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l);
+    split_publish(sm, m, l);
+    if (hq == 0) {
+      const float mg = sm.ml[w][hr][0];
+      a.ws_ml[(pbase + 16 * w + hr) * 2 + 0] = mg;
+      a.ws_ml[(pbase + 16 * w + hr) * 2 + 1] = (mg == -INFINITY) ? 0.f : sm.ml[w][hr][1];
+    }
+    return;
+  }
+
+  // accumulating wave j: partial O of the four groups over columns 128 j ..
+  const uint32_t j = w - kSplitGroups;
   f32x4_t o[kSplitGroups][kSplitNb];
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g)
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
   __syncthreads();
-
-  split_stream(a.ra, sm, base + r0, r1 - r0, a.scale_log2,
-               [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l, o);
-
-  split_publish(sm, m, l);
-  const size_t pbase = ((size_t)b * a.n_splits + sp) * a.n_heads + g0 * 16;
+  value_stream(a.ra, sm, base + r0, r1 - r0, o);
+  split_publish_wait();
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g) {
-    float* dst = a.ws_acc + (pbase + 16 * g + hr) * IRM_D_LATENT + kSplitCols * w + 4 * hq;
+    float* dst = a.ws_acc + (pbase + 16 * g + hr) * IRM_D_LATENT + kSplitCols * j + 4 * hq;
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb)
       *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[g][nb][0], o[g][nb][1], o[g][nb][2], o[g][nb][3]);
-  }
-  if (w == 0 && hq == 0) {
-#pragma unroll
-    for (int g = 0; g < kSplitGroups; ++g) {
-      const float mg = sm.ml[g][hr][0];
-      a.ws_ml[(pbase + 16 * g + hr) * 2 + 0] = mg;
-      a.ws_ml[(pbase + 16 * g + hr) * 2 + 1] = (mg == -INFINITY) ? 0.f : sm.ml[g][hr][1];
-    }
   }
 }
 
@@ -331,7 +336,7 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
   const uint64_t grid = (bs + 7) / 8 * 8 * (shared ? G / kSplitGroups : G);
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");
   if (shared)
-    hipLaunchKernelGGL(decode_shared_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_shared_kernel, dim3((uint32_t)grid), dim3(kRoleThreads), 0, s, a);
   else
     hipLaunchKernelGGL(decode_private_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   irm_status st = launch_check("irm_mla_decode: split kernel");

@@ -15,9 +15,10 @@ using namespace irm::dev;
 
 // ---------------------------------------------------------------------------
 // Four queries per workgroup, one 16-head group: the four (query, 16 heads)
-// groups share every 32-row tile of the causal range of the last query
-// (split_stream).  Wave w scores query w and
-// accumulates output columns 128 w .. 128 w + 127 of all four.
+// groups share every 32-row tile of the causal range of the last query.
+// Scoring wave s scores query s; accumulating wave j copies and rotates
+// slice j of every tile and sums output columns 128 j .. 128 j + 127 of all
+// four queries (score_stream / value_stream).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kQueriesPerBlock = kSplitGroups;
 
@@ -34,43 +35,52 @@ struct PrefillArgs {
   InvFreq f;
 };
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) SplitSmem sm;
 
   const uint32_t hg = blockIdx.x % a.n_groups;
   const uint32_t q0 = (blockIdx.x / a.n_groups) * kQueriesPerBlock;
-  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6, hq = lane >> 4, hr = lane & 15;
+  const uint32_t lane = threadIdx.x & 63, w = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t head = hg * 16 + hr;
   const uint32_t q_last = min(a.n_q, q0 + kQueriesPerBlock) - 1;
   const uint32_t rows = (uint32_t)a.q_pos0 + q_last + 1;  // KV rows this workgroup visits
-  const uint32_t qi = q0 + w;
-  const int64_t lim = qi < a.n_q ? (int64_t)a.q_pos0 + qi : -1;  // last visible row of this wave's query
-
-  bf16x8_t qb[18];
-  load_q(a.q_lat, a.q_rope, min(qi, q_last), a.n_heads, head, qb);
   fill_omega(sm.s.omega, a.f);
+
+  if (w < kSplitGroups) {  // scoring wave: query q0 + w
+    const uint32_t qi = q0 + w;
+    const int64_t lim = qi < a.n_q ? (int64_t)a.q_pos0 + qi : -1;  // last visible row of the query
+    bf16x8_t qb[18];
+    load_q<false>(a.q_lat, a.q_rope, min(qi, q_last), a.n_heads, head, qb);
+    float m = -INFINITY, l = 0.f;
+    __syncthreads();
+    score_stream(sm, rows, a.scale_log2,
+                 [&](uint32_t t, uint32_t) -> int32_t {
+                   const int64_t last = lim - (int64_t)t * kTileRows;
+                   return last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last);
+                 },
+                 qb, m, l);
+    split_publish(sm, m, l);
+    if (a.lse && qi < a.n_q && hq == 0)
+      a.lse[(size_t)qi * a.n_heads + head] = (sm.ml[w][hr][0] + log2f(sm.ml[w][hr][1])) * kLn2;
+    return;
+  }
+
+  // accumulating wave j: columns 128 j .. 128 j + 127 of the four queries
+  const uint32_t j = w - kSplitGroups;
   f32x4_t o[kSplitGroups][kSplitNb];
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g)
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
   __syncthreads();
-
-  split_stream(a.ra, sm, a.seq_base[0], rows, a.scale_log2,
-               [&](uint32_t t, uint32_t) -> int32_t {
-                 const int64_t last = lim - (int64_t)t * kTileRows;
-                 return last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last);
-               },
-               qb, m, l, o);
-
-  split_publish(sm, m, l);
+  value_stream(a.ra, sm, a.seq_base[0], rows, o);
+  split_publish_wait();
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g) {
     const uint32_t qg = q0 + g;
     if (qg >= a.n_q) break;
     const float inv = 1.f / sm.ml[g][hr][1];
-    uint16_t* op = a.out + ((size_t)qg * a.n_heads + head) * IRM_D_LATENT + kSplitCols * w + 4 * hq;
+    uint16_t* op = a.out + ((size_t)qg * a.n_heads + head) * IRM_D_LATENT + kSplitCols * j + 4 * hq;
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) {
       uint2 v;
@@ -78,8 +88,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
       v.y = pack_bf16(o[g][nb][2] * inv, o[g][nb][3] * inv);
       *reinterpret_cast<uint2*>(op + 16 * nb) = v;
     }
-    if (a.lse && w == 0 && hq == 0)
-      a.lse[(size_t)qg * a.n_heads + head] = (sm.ml[g][hr][0] + log2f(sm.ml[g][hr][1])) * kLn2;
   }
 }
 
@@ -105,7 +113,7 @@ irm_status launch_prefill(const irm_table* t, const void* q_lat, const void* q_r
   for (int i = 0; i < (int)kPairs; ++i) a.f.w[i] = t->inv_freq[i];
   const uint64_t grid = (uint64_t)(n_q + kQueriesPerBlock - 1) / kQueriesPerBlock * a.n_groups;
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_prefill_tail: grid too large");
-  hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kRoleThreads), 0, s, a);
   return launch_check("irm_mla_prefill_tail");
 }
 

@@ -352,3 +352,28 @@ def test_error_paths():
     with pytest.raises(irm.IrmError) as e:
         irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(dev_buf=small)
     assert e.value.code == "EWORKSPACE"
+
+
+def test_decode_workspace_reuse_across_split_counts():
+    """One workspace serves consecutive decodes with different split counts;
+    no call may depend on what an earlier call left in it."""
+    import torch
+    w = random_table(13, [3000, 1200, 40], heads=16)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    need = max(irm.decode_workspace_bytes(t, w.n_heads, S) for S in (2, 3, 4, 8, 16))
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")  # arbitrary prior contents
+    first = None
+    for S in (4, 2, 8, 16, 3, 4, 4):
+        out, lse = irm.mla_decode(ql, qr, t, pool, n_splits=S, scale=w.scale, want_lse=True, workspace=ws)
+        _sync()
+        o = oracle.bf16_to_f64(irm.from_device_bf16(out))
+        assert rel_l2(o, o_ref) <= ATTN_TOL, S
+        assert np.max(np.abs(lse.cpu().numpy() - l_ref)) <= LSE_TOL, S
+        if S == 4:
+            if first is None:
+                first = o
+            else:
+                assert np.array_equal(o, first)
