@@ -565,18 +565,16 @@ __device__ __forceinline__ void slice_rot_store(unsigned char* kr, uint32_t row0
 // either covers the other's LDS, copy and barrier waits with its MFMAs.
 //
 // Iteration t (0 <= t <= nt) ends with one barrier.  Scorers: tile t (t < nt)
-// -> P under parity t.  Accumulators: PV of tile t-1 (t >= 1) from the P
-// published one iteration earlier, interleaved with the copies of tile t+2;
-// the row map of tile t+4; wait for tile t+1 and rotate their slice of it.
+// -> P under parity t.  Accumulators: wait for tile t+1 and rotate their
+// slice of it, PV of tile t-1 (t >= 1) from the P published one iteration
+// earlier, interleaved with the copies of tile t+2; the row map of tile t+4.
 // Stages in use during iteration t: t-1 (PV), t (QK), t+1 (rotate), t+2
 // (copies in flight).  Copies of tiles past the end re-read the last tile
-// into the free stage, so every iteration issues kTileCopies copies per
-// accumulator and "tile t+1 has landed" is "at most kTileCopies outstanding"
-// (the copies of tile t+2 and the row map of tile t+4).  Barriers per call:
-// nt + 2 on both sides, none when nt = 0.
+// into the free stage, so every iteration issues the same copies per
+// accumulator (k_r, 8 c_KV rows, row map) and the waits count them.
+// Barriers per call: nt + 2 on both sides, none when nt = 0.
 // ---------------------------------------------------------------------------
 constexpr int kRoleThreads = 2 * kThreads;
-constexpr int kTileCopies = kTileSlice + 1 + 1;  // c_KV rows, k_r, row map
 
 // Wave index as a scalar: roles branch on it without divergence.
 __device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -639,11 +637,11 @@ __device__ __forceinline__ void score_stream(SplitSmem& sm, uint32_t n, float c,
 // Accumulator side: rows [g_begin, g_begin + n) of the assembled sequence.
 // sm.s.omega must be visible.  The row-map data an iteration needs (copy
 // sources of tile t+2, deltas of tile t+1) is read into registers one
-// iteration ahead, so that the only LDS round trips on the way from one
-// barrier to the next are the P / C^T fragments and the k_r to rotate.
+// iteration ahead, so that the only LDS round trip on the way from one
+// barrier to the next is the one for the P / C^T fragments and the k_r to
+// rotate.
 __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
                                              f32x4_t (&o)[kSplitGroups][kSplitNb]) {
-  static_assert(kTileCopies == 10, "the waits below count 10 copies per iteration");
   const uint32_t lane = threadIdx.x & 63, j = wave_id() - kSplitGroups, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
@@ -657,26 +655,50 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
   SliceCopies cp;  // copy sources of tile t+2
   int32_t d1;      // delta of this lane's row of tile t+1
 
-  // kB: tile t-1 exists (t >= 1)
+  // Iteration t: wait for tile t+1 and read the P / C^T fragments and the
+  // k_r of tile t+1 in one go.  The first half of the PV MFMAs of tile t-1
+  // carries the copies of tile t+2; then the rotated k_r is written back and
+  // the row-map data of the next iteration read, while the second half runs.
+  // The row map of tile t+4 goes out last.  kB: tile t-1 exists (t >= 1).
   auto iteration = [&](uint32_t t, auto kB) {
     constexpr bool B = decltype(kB)::value;
     unsigned char* nx = stage(t + 2);
+    unsigned char* sr = stage(t + 1) + kTileKr;
+    const bool rot = t + 1 < nt;
+    const bool table = rot && slice_trig_ready(ws, sm.s.omega, d1, cd);
+    // Tile t+1 has landed: after its copies only the row map of tile t+3
+    // went out (t >= 1); at t = 0 nothing did.
+    wait_dma_but<B ? 1 : 0>();
+    const SliceRot rt = slice_rot_load(ws, sr, row0, d1, cd);
+    const int32_t d_rot = d1;
+    copy_kr(ra, cp, nx + kTileKr, row0);
+    auto mid = [&]() {
+      if (table) slice_rot_store(sr, row0, rt);
+      // All 9 copies of tile t+2 are out; the row map of tile t+3, issued
+      // before them, has landed.
+      wait_dma_but<kTileSlice + 1>();
+      cp = prep_copies(ra, ws.rm[(t + 3) % kTileRm]);
+      d1 = delta(t + 2);
+    };
     if constexpr (B) {
       const uint32_t pb = (t - 1) & 1;
       const uint4 scaled = *reinterpret_cast<const uint4*>(sm.scaled[pb]);
-      bf16x8_t pf[kSplitGroups], cf[kSplitNb];
+      bf16x8_t pf[kSplitGroups];
 #pragma unroll
       for (int g = 0; g < kSplitGroups; ++g) pf[g] = __builtin_bit_cast(bf16x8_t, sm.pfrag[pb][g][lane]);
       typedef short i16x8_t __attribute__((ext_vector_type(8)));
       const CtBases c0 = ct_bases(stage(t - 1), 0);
-#pragma unroll
-      for (int nb = 0; nb < kSplitNb; ++nb) {
+      auto read_cf = [&](int nb) {
         const int nn = kSplitNb * j + nb;
         const i16x4_t lo = ct_read(c0, nn);
         const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_i16x4_ptr)(c0.b[nn & 7] + 256 * (nn >> 3) + 16 * kCkvBytes));
-        cf[nb] = __builtin_bit_cast(bf16x8_t, (i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
-      }
+        return __builtin_bit_cast(bf16x8_t, (i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
+      };
+      constexpr int kCfAhead = 4;  // C^T fragments in registers at a time
+      bf16x8_t cf[kCfAhead];
+#pragma unroll
+      for (int nb = 0; nb < kCfAhead; ++nb) cf[nb] = read_cf(nb);
       if (scaled.x | scaled.y | scaled.z | scaled.w) {
 #pragma unroll
         for (int g = 0; g < kSplitGroups; ++g) {
@@ -685,32 +707,27 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
           for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] *= a;
         }
       }
+      static_assert(kSplitNb == kTileSlice, "two copies ride on each of the first half of the column blocks");
 #pragma unroll
       for (int nb = 0; nb < kSplitNb; ++nb) {
-        copy_ckv(ra, cp, nb, nx, row0);
+        if (nb < kSplitNb / 2) {
+          copy_ckv(ra, cp, 2 * nb, nx, row0);
+          copy_ckv(ra, cp, 2 * nb + 1, nx, row0);
+        }
+        const bf16x8_t c = cf[nb % kCfAhead];
+        if (nb + kCfAhead < kSplitNb) cf[nb % kCfAhead] = read_cf(nb + kCfAhead);
 #pragma unroll
         for (int g = 0; g < kSplitGroups; ++g)
-          o[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf[nb], pf[g], o[g][nb], 0, 0, 0);
+          o[g][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c, pf[g], o[g][nb], 0, 0, 0);
+        if (nb == kSplitNb / 2 - 1) mid();
       }
     } else {
 #pragma unroll
       for (int k = 0; k < kTileSlice; ++k) copy_ckv(ra, cp, k, nx, row0);
+      mid();
     }
-    copy_kr(ra, cp, nx + kTileKr, row0);
     slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);
-    const bool rot = t + 1 < nt;
-    const bool table = rot && slice_trig_ready(ws, sm.s.omega, d1, cd);
-    wait_dma_but<kTileCopies>();  // tile t+1 and the row map of tile t+3 have landed
-    const int32_t d_rot = d1;
-    cp = prep_copies(ra, ws.rm[(t + 3) % kTileRm]);
-    d1 = delta(t + 2);
-    if (rot) {
-      unsigned char* sr = stage(t + 1) + kTileKr;
-      if (table)
-        slice_rot_store(sr, row0, slice_rot_load(ws, sr, row0, d_rot, cd));
-      else
-        slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d_rot, cd);
-    }
+    if (rot && !table) slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d_rot, cd);
     __syncthreads();
   };
 
@@ -724,7 +741,7 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
   }
   cp = prep_copies(ra, ws.rm[2]);
   d1 = delta(1);
-  wait_dma_but<kTileCopies - 1>();  // tile 0 has landed (tile 1's copies may be outstanding)
+  wait_dma_but<kTileSlice + 1>();  // tile 0 has landed (tile 1's copies may be outstanding)
   slice_rotate<kTileSlice>(ws, stage(0) + kTileKr, row0, sm.s.omega, delta(0), cd);
   __syncthreads();
   iteration(0, std::false_type{});
