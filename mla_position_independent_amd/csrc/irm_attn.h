@@ -575,21 +575,33 @@ __device__ __forceinline__ void slice_rot_store(unsigned char* kr, uint32_t row0
 // Barriers per call: nt + 2 on both sides, none when nt = 0.
 // ---------------------------------------------------------------------------
 constexpr int kRoleThreads = 2 * kThreads;
+constexpr int kScoreRows = 6;  // c_KV rows of each slice that the scorer copies
+static_assert(kScoreRows >= 0 && kScoreRows < kTileSlice && kScoreRows <= 16, "split of the slice copies");
 
 // Wave index as a scalar: roles branch on it without divergence.
 __device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Scorer side.  last(t, nrows) is the last visible tile row of the wave's
-// group in tile t (nrows rows of the tile exist).
+// group in tile t (nrows rows of the tile exist).  Scorer s also copies the
+// first kScoreRows c_KV rows of slice s of tile t+2 during iteration t (the
+// accumulator of that slice copies the rest, its k_r and row maps), from the
+// row-map records the accumulator published one barrier earlier, and waits
+// for them before the barrier that ends iteration t+1.
 template <class Last>
-__device__ __forceinline__ void score_stream(SplitSmem& sm, uint32_t n, float c, Last&& last,
+__device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t n, float c, Last&& last,
                                              const bf16x8_t (&qb)[18], float& m, float& l) {
   const uint32_t lane = threadIdx.x & 63, s = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
+  const WaveSlots<kTileRm, kTileSlice>& ws = sm.s.slots[s];
+  const uint32_t row0 = kTileSlice * s;
   __syncthreads();  // tile 0 is in place
   const uint32_t ln = opaque(lane), q = ln >> 4, rr = ln & 15;
   for (uint32_t t = 0; t < nt; ++t) {
+    uint32_t src[kScoreRows > 0 ? kScoreRows : 1];
+    unsigned char* nx = sm.s.stage[(t + 2) % kStages];
+#pragma unroll
+    for (int k = 0; k < kScoreRows; ++k) src[k] = min(ws.rm[(t + 2) % kTileRm][k].x, ra.pool_last);
     const unsigned char* sa = sm.s.stage[t % kStages];
     const unsigned char* rowp = sa + rr * kCkvBytes + ((q ^ (rr & 3)) << 4);
     const unsigned char* base[4];
@@ -614,6 +626,10 @@ __device__ __forceinline__ void score_stream(SplitSmem& sm, uint32_t n, float c,
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) {
       if (kk + kAhead < 18) read(kk + kAhead, ring[(kk + kAhead) % (kAhead + 1)]);
+      if (kk >= 2 && kk - 2 < kScoreRows) {
+        const uint32_t k = kk - 2, r = row0 + k;
+        dma16(ra.pool + (size_t)src[k] * kRowBytes + ((lane ^ (r & 15)) << 4), lds_addr(nx + r * kCkvBytes));
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[kk % (kAhead + 1)][j], qb[kk], acc[j], 0, 0, 0);
@@ -629,9 +645,11 @@ __device__ __forceinline__ void score_stream(SplitSmem& sm, uint32_t n, float c,
     sm.pfrag[t & 1][s][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
     if (hq == 0) sm.alpha[t & 1][s][hr] = alpha;
     if (lane == 0) sm.scaled[t & 1][s] = moved ? 1u : 0u;
+    wait_dma_but<kScoreRows>();  // this wave's rows of tile t+1 have landed
     __syncthreads();
   }
   __syncthreads();  // the accumulators' last PV
+  wait_dma_all();
 }
 
 // Accumulator side: rows [g_begin, g_begin + n) of the assembled sequence.
@@ -674,9 +692,9 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
     copy_kr(ra, cp, nx + kTileKr, row0);
     auto mid = [&]() {
       if (table) slice_rot_store(sr, row0, rt);
-      // All 9 copies of tile t+2 are out; the row map of tile t+3, issued
-      // before them, has landed.
-      wait_dma_but<kTileSlice + 1>();
+      // This iteration's copies of tile t+2 are out; the row map of tile
+      // t+3, issued before them, has landed.
+      wait_dma_but<kTileSlice - kScoreRows + 1>();
       cp = prep_copies(ra, ws.rm[(t + 3) % kTileRm]);
       d1 = delta(t + 2);
     };
@@ -707,13 +725,12 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
           for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] *= a;
         }
       }
-      static_assert(kSplitNb == kTileSlice, "two copies ride on each of the first half of the column blocks");
 #pragma unroll
       for (int nb = 0; nb < kSplitNb; ++nb) {
-        if (nb < kSplitNb / 2) {
-          copy_ckv(ra, cp, 2 * nb, nx, row0);
-          copy_ckv(ra, cp, 2 * nb + 1, nx, row0);
-        }
+        // the copies ride on the first half of the column blocks
+#pragma unroll
+        for (int k = kScoreRows; k < kTileSlice; ++k)
+          if ((k - kScoreRows) * (kSplitNb / 2) / (kTileSlice - kScoreRows) == nb) copy_ckv(ra, cp, k, nx, row0);
         const bf16x8_t c = cf[nb % kCfAhead];
         if (nb + kCfAhead < kSplitNb) cf[nb % kCfAhead] = read_cf(nb + kCfAhead);
 #pragma unroll
@@ -723,7 +740,7 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < kTileSlice; ++k) copy_ckv(ra, cp, k, nx, row0);
+      for (int k = kScoreRows; k < kTileSlice; ++k) copy_ckv(ra, cp, k, nx, row0);
       mid();
     }
     slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);

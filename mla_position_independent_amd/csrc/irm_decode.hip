@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeAr
     load_q<false>(a.q_lat, a.q_rope, b, a.n_heads, (g0 + w) * 16 + hr, qb);
     float m = -INFINITY, l = 0.f;
     __syncthreads();
-    score_stream(sm, r1 - r0, a.scale_log2,
+    score_stream(a.ra, sm, r1 - r0, a.scale_log2,
                  [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l);
     split_publish(sm, m, l);
     if (hq == 0) {

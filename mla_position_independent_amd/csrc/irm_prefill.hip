@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
     load_q<false>(a.q_lat, a.q_rope, min(qi, q_last), a.n_heads, head, qb);
     float m = -INFINITY, l = 0.f;
     __syncthreads();
-    score_stream(sm, rows, a.scale_log2,
+    score_stream(a.ra, sm, rows, a.scale_log2,
                  [&](uint32_t t, uint32_t) -> int32_t {
                    const int64_t last = lim - (int64_t)t * kTileRows;
                    return last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last);
