@@ -212,6 +212,10 @@ def test_decode_tiny():
     (4, 128, [1000, 777], 4),
     (5, 48, [3000], 7),
     (6, 16, [5], 64),            # more splits than rows: empty splits
+    (7, 64, [1, 2, 31, 33, 64, 65], 0),   # 64-head blocks: ragged, sub-tile sequences
+    (8, 64, [5], 64),            # 64-head blocks, empty splits
+    (9, 128, [3000, 40], 16),
+    (10, 96, [257], 2),          # six 16-head groups: per-group workgroups
 ])
 def test_decode_random(seed, heads, lens, splits):
     w = random_table(seed, lens, heads=heads, p_hit=0.7, prefix_frac=0.3)
@@ -221,6 +225,42 @@ def test_decode_random(seed, heads, lens, splits):
     assert np.max(np.abs(l - l_ref)) <= LSE_TOL
     for b in range(w.n_seq):          # every sequence, not only the aggregate
         assert rel_l2(o[b], o_ref[b]) <= ATTN_TOL, b
+
+
+def _tiny_chunks(rng):
+    return int(rng.integers(1, 8))
+
+
+@pytest.mark.parametrize("heads", [16, 64])
+def test_decode_short_chunks(heads):
+    """Chunks of 1..7 rows: most 8-row slices hold three or more deltas, which
+    the per-wave trig table (two deltas) cannot cover."""
+    w = random_table(31, [600, 257, 40], heads=heads, p_hit=0.9, len_fn=_tiny_chunks)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    for S in (1, 5):
+        o, l = _gpu_decode(w, S)
+        assert rel_l2(o, o_ref) <= ATTN_TOL, S
+        assert np.max(np.abs(l - l_ref)) <= LSE_TOL, S
+
+
+def _scaled_queries(w, f):
+    """Queries times a power of two (exact in bf16): larger score spread, so
+    the running maximum moves past the lazy-rescale slack mid-stream."""
+    from synth.workloads import bf16_bits_from_f32
+    w.q_lat = bf16_bits_from_f32((oracle.bf16_to_f64(w.q_lat) * f).astype(np.float32))
+    w.q_rope = bf16_bits_from_f32((oracle.bf16_to_f64(w.q_rope) * f).astype(np.float32))
+    return w
+
+
+@pytest.mark.parametrize("heads", [16, 64])
+def test_decode_rescale_paths(heads):
+    """The lse bound scales with |q_rope| (the score error of the bf16 k_r is
+    linear in it), so it is taken four times wider here."""
+    w = _scaled_queries(random_table(32, [3000, 1100], heads=heads, p_hit=0.7), 4.0)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    o, l = _gpu_decode(w, 2)
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= 4.0 * LSE_TOL
 
 
 def test_decode_split_invariance_and_determinism():
@@ -302,6 +342,15 @@ def test_prefill_random(seed, heads, N, nq):
     assert np.max(np.abs(l - l_ref)) <= LSE_TOL
     for i in (0, nq - 1):
         assert rel_l2(o[i], o_ref[i]) <= ATTN_TOL
+
+
+def test_prefill_short_chunks_and_rescale():
+    w = _scaled_queries(random_table(33, [900], heads=16, p_hit=0.9, len_fn=_tiny_chunks, n_q=70,
+                                     kind="prefill"), 4.0)
+    o, l = _gpu_prefill(w)
+    o_ref, l_ref = _oracle_prefill(w, None)
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= 4.0 * LSE_TOL  # queries times 4, as in the decode case
 
 
 def test_prefill_last_query_equals_decode():
