@@ -43,11 +43,20 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
 
 // Wave-wide copy: lane l's 16 bytes at g land at LDS address lds + 16 l
 // (one wait state between the M0 write and the LDS-DMA load).
+// kStream marks data read exactly once (the non-temporal policy keeps it
+// from displacing rows that other workgroups still read from the caches).
+template <bool kStream = false>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "m0");
+  if constexpr (kStream)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "m0");
 }
 
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -281,8 +290,9 @@ __device__ __forceinline__ void slice_issue_rowmap(const StreamArgs& ra, uint32_
 }
 
 // Data of the slice described by rec into tile rows row0.. of the stage with
-// c_KV at ckv and k_r at kr.  Pool rows are clamped so that a corrupted map
-// yields wrong values, never a fault.
+// c_KV at ckv and k_r at kr, streamed (every row is read once per launch by
+// the workgroup that copies it).  Pool rows are clamped so that a corrupted
+// map yields wrong values, never a fault.
 template <int R>
 __device__ __forceinline__ void slice_issue_data(const StreamArgs& ra, const uint4* rec, unsigned char* ckv,
                                                  unsigned char* kr, uint32_t row0) {
@@ -296,13 +306,13 @@ __device__ __forceinline__ void slice_issue_data(const StreamArgs& ra, const uin
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const uint32_t r = row0 + k;
-    dma16(ra.pool + (size_t)src[k] * kRowBytes + ((l ^ (r & 15)) << 4), lds_addr(ckv + r * kCkvBytes));
+    dma16<true>(ra.pool + (size_t)src[k] * kRowBytes + ((l ^ (r & 15)) << 4), lds_addr(ckv + r * kCkvBytes));
   }
 #pragma unroll
   for (int h = 0; h < R / 8; ++h) {
     const uint32_t r = row0 + 8 * h + (l >> 3);
-    dma16(ra.pool + (size_t)ksrc[h] * kRowBytes + kCkvBytes + (((l & 7) ^ ((r >> 1) & 7)) << 4),
-          lds_addr(kr + (row0 + 8 * h) * kKrBytes));
+    dma16<true>(ra.pool + (size_t)ksrc[h] * kRowBytes + kCkvBytes + (((l & 7) ^ ((r >> 1) & 7)) << 4),
+                lds_addr(kr + (row0 + 8 * h) * kKrBytes));
   }
 }
 

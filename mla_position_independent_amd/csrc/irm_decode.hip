@@ -112,6 +112,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
   WaveSlots<kPrivRm, kPrivRows>& ws = sm.slots[wave];
   auto g0 = [&](uint32_t t) { return g_begin + min(t, nt - 1) * kPrivRows; };
 
+  // The row maps of the first slices go out before the query loads, so that
+  // both round trips overlap (the loads' waits cover the older copies).
+  if (nt > 0)
+    for (uint32_t t = 0; t < 3; ++t) slice_issue_rowmap<kPrivRows>(a.ra, g0(t), ws.rm[t]);
   bf16x8_t qb[18];
   load_q(a.q_lat, a.q_rope, b, a.n_heads, head, qb);
   fill_omega(sm.omega, a.f);
@@ -123,7 +127,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
   __syncthreads();
 
   if (nt > 0) {
-    for (uint32_t t = 0; t < 3; ++t) slice_issue_rowmap<kPrivRows>(a.ra, g0(t), ws.rm[t]);
     wait_dma_all();
     slice_issue_data<kPrivRows>(a.ra, ws.rm[0], sm.stage[wave][0], sm.stage[wave][0] + kPrivStageKr, 0);
     for (uint32_t t = 0; t < nt; ++t) {
