@@ -270,17 +270,21 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
                                                              uint32_t n_heads, uint32_t n_splits) {
   const uint32_t bh = blockIdx.x;
   const uint32_t b = bh / n_heads, h = bh % n_heads;
+  const size_t p0 = (size_t)b * n_splits * n_heads + h;  // partial of split s: p0 + s * n_heads
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml);
   float mx = -INFINITY;
-  for (uint32_t s = 0; s < n_splits; ++s)
-    mx = fmaxf(mx, ws_ml[(((size_t)b * n_splits + s) * n_heads + h) * 2]);
+#pragma unroll 8
+  for (uint32_t s = 0; s < n_splits; ++s) mx = fmaxf(mx, ml[p0 + (size_t)s * n_heads].x);
+  // Every split slot holds finite partials (zeros for a split without rows,
+  // whose maximum is -inf and weight 0), so all loads go out unconditionally.
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
   for (uint32_t s = 0; s < n_splits; ++s) {
-    const size_t p = ((size_t)b * n_splits + s) * n_heads + h;
-    const float ms = ws_ml[p * 2];
-    if (ms == -INFINITY) continue;
-    const float f = exp2f(ms - mx);
-    L += f * ws_ml[p * 2 + 1];
+    const size_t p = p0 + (size_t)s * n_heads;
+    const float2 v2 = ml[p];
+    const float f = (v2.x == -INFINITY) ? 0.f : exp2f(v2.x - mx);
+    L += f * v2.y;
     const float4 v = reinterpret_cast<const float4*>(ws_acc + p * IRM_D_LATENT)[threadIdx.x];
     acc.x += f * v.x;
     acc.y += f * v.y;
