@@ -263,6 +263,12 @@ __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeAr
 // ---------------------------------------------------------------------------
 // split-KV decode, pass 2
 // ---------------------------------------------------------------------------
+// One workgroup per (sequence, head), one float4 of the 512 columns per
+// thread.  kMax > 0: at most kMax splits, every load issued before any
+// arithmetic; kMax = 0: any count, in batches.  Every split slot holds finite
+// partials (zeros for a split without rows, whose maximum is -inf and whose
+// weight is 0), so no load depends on another split's values.
+template <int kMax>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws_acc,
                                                              const float* __restrict__ ws_ml,
                                                              uint16_t* __restrict__ out,
@@ -272,24 +278,36 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
   const uint32_t b = bh / n_heads, h = bh % n_heads;
   const size_t p0 = (size_t)b * n_splits * n_heads + h;  // partial of split s: p0 + s * n_heads
   const float2* ml = reinterpret_cast<const float2*>(ws_ml);
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (uint32_t s = 0; s < n_splits; ++s) mx = fmaxf(mx, ml[p0 + (size_t)s * n_heads].x);
-  // Every split slot holds finite partials (zeros for a split without rows,
-  // whose maximum is -inf and weight 0), so all loads go out unconditionally.
-  float L = 0.f;
+  auto acc_of = [&](uint32_t s) {
+    return reinterpret_cast<const float4*>(ws_acc + (p0 + (size_t)s * n_heads) * IRM_D_LATENT)[threadIdx.x];
+  };
+  float mx = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (uint32_t s = 0; s < n_splits; ++s) {
-    const size_t p = p0 + (size_t)s * n_heads;
-    const float2 v2 = ml[p];
-    const float f = (v2.x == -INFINITY) ? 0.f : exp2f(v2.x - mx);
-    L += f * v2.y;
-    const float4 v = reinterpret_cast<const float4*>(ws_acc + p * IRM_D_LATENT)[threadIdx.x];
+  auto add = [&](float2 m2, float4 v) {
+    const float f = (m2.x == -INFINITY) ? 0.f : exp2f(m2.x - mx);
+    L += f * m2.y;
     acc.x += f * v.x;
     acc.y += f * v.y;
     acc.z += f * v.z;
     acc.w += f * v.w;
+  };
+  if constexpr (kMax > 0) {
+    float2 m2[kMax];
+    float4 v[kMax];
+#pragma unroll
+    for (int s = 0; s < kMax; ++s) {
+      m2[s] = (uint32_t)s < n_splits ? ml[p0 + (size_t)s * n_heads] : make_float2(-INFINITY, 0.f);
+      v[s] = (uint32_t)s < n_splits ? acc_of(s) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int s = 0; s < kMax; ++s) mx = fmaxf(mx, m2[s].x);
+#pragma unroll
+    for (int s = 0; s < kMax; ++s) add(m2[s], v[s]);
+  } else {
+#pragma unroll 8
+    for (uint32_t s = 0; s < n_splits; ++s) mx = fmaxf(mx, ml[p0 + (size_t)s * n_heads].x);
+#pragma unroll 8
+    for (uint32_t s = 0; s < n_splits; ++s) add(ml[p0 + (size_t)s * n_heads], acc_of(s));
   }
   const float inv = 1.f / L;
   uint2 w;
@@ -348,8 +366,14 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
     hipLaunchKernelGGL(decode_private_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   irm_status st = launch_check("irm_mla_decode: split kernel");
   if (st != IRM_OK) return st;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(t->n_seq * n_heads), dim3(128), 0, s, ws_acc, ws_ml,
-                     static_cast<uint16_t*>(out), lse, n_heads, n_splits);
+  const dim3 cgrid(t->n_seq * n_heads), cblock(128);
+  uint16_t* o16 = static_cast<uint16_t*>(out);
+  if (n_splits <= 4)
+    hipLaunchKernelGGL(decode_combine_kernel<4>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_splits);
+  else if (n_splits <= 16)
+    hipLaunchKernelGGL(decode_combine_kernel<16>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_splits);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<0>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_splits);
   return launch_check("irm_mla_decode: combine kernel");
 }
 
