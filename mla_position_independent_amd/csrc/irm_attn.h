@@ -569,20 +569,31 @@ __device__ __forceinline__ void slice_rot_store(unsigned char* kr, uint32_t row0
 // Role-split streaming of split tiles: eight waves per workgroup, two per
 // SIMD.  Waves 0..3 score: wave s holds Q of group s, computes S^T of every
 // tile, runs the online softmax and publishes P and the rescale factors.
-// Waves 4..7 accumulate: wave 4+j copies and rotates slice j (rows 8j..8j+7)
-// of every tile and accumulates O of all four groups over output columns
-// 128 j .. 128 j + 127.  Each SIMD thus runs one wave of each kind, and
-// either covers the other's LDS, copy and barrier waits with its MFMAs.
+// Waves 4..7 accumulate: wave 4+j sums O of all four groups over output
+// columns 128 j .. 128 j + 127.  Each SIMD thus runs one wave of each kind,
+// and either covers the other's LDS, copy and barrier waits with its MFMAs.
+// Slice j of a tile (rows 8j..8j+7) is copied by scorer j (its first
+// kScoreRows c_KV rows) and accumulator j (the other c_KV rows, the k_r and
+// the row maps), and rotated by accumulator j.
 //
-// Iteration t (0 <= t <= nt) ends with one barrier.  Scorers: tile t (t < nt)
-// -> P under parity t.  Accumulators: wait for tile t+1 and rotate their
-// slice of it, PV of tile t-1 (t >= 1) from the P published one iteration
-// earlier, interleaved with the copies of tile t+2; the row map of tile t+4.
-// Stages in use during iteration t: t-1 (PV), t (QK), t+1 (rotate), t+2
-// (copies in flight).  Copies of tiles past the end re-read the last tile
-// into the free stage, so every iteration issues the same copies per
-// accumulator (k_r, 8 c_KV rows, row map) and the waits count them.
-// Barriers per call: nt + 2 on both sides, none when nt = 0.
+// Iteration t (0 <= t <= nt) ends with one barrier.  Scorers (t < nt):
+// scores of tile t with their copies of tile t+2 between the MFMAs, softmax,
+// P under parity t, then a wait for their copies of tile t+1.  Accumulators:
+// wait for tile t+1 and rotate their slice of it, PV of tile t-1 (t >= 1)
+// from the P published one iteration earlier with their copies of tile t+2
+// between the MFMAs, the row map of tile t+4.  Stages in use during
+// iteration t: t-1 (PV), t (QK), t+1 (rotate), t+2 (copies in flight).
+// Copies of tiles past the end re-read the last tile into the free stage,
+// so every iteration issues the same copies per wave and the waits count
+// them.  Barriers per call: nt + 2 on both sides, none when nt = 0.
+//
+// Segments: with seg_tiles > 0 the rows form consecutive segments of
+// seg_tiles tiles (the last one may be shorter), each with its own softmax
+// state.  The scorers hand (m, l) of a segment to seg_end(k, m, l) after its
+// last tile's softmax and restart from -inf; the accumulators hand O to
+// seg_end(k, o) after that tile's PV and restart from zero.  The first tile
+// of a segment always moves the reference maximum away from -inf, and its
+// rescale factor (0) then meets the zeroed O.
 // ---------------------------------------------------------------------------
 constexpr int kRoleThreads = 2 * kThreads;
 constexpr int kScoreRows = 6;  // c_KV rows of each slice that the scorer copies
@@ -597,9 +608,10 @@ __device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirs
 // accumulator of that slice copies the rest, its k_r and row maps), from the
 // row-map records the accumulator published one barrier earlier, and waits
 // for them before the barrier that ends iteration t+1.
-template <class Last>
+template <class Last, class SegEnd>
 __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t n, float c, Last&& last,
-                                             const bf16x8_t (&qb)[18], float& m, float& l) {
+                                             const bf16x8_t (&qb)[18], float& m, float& l, uint32_t seg_tiles,
+                                             SegEnd&& seg_end) {
   const uint32_t lane = threadIdx.x & 63, s = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
@@ -655,6 +667,11 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
     sm.pfrag[t & 1][s][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
     if (hq == 0) sm.alpha[t & 1][s][hr] = alpha;
     if (lane == 0) sm.scaled[t & 1][s] = moved ? 1u : 0u;
+    if (seg_tiles && ((t + 1) % seg_tiles == 0 || t + 1 == nt)) {  // last tile of a segment
+      seg_end(t / seg_tiles, m, l);
+      m = -INFINITY;
+      l = 0.f;
+    }
     wait_dma_but<kScoreRows>();  // this wave's rows of tile t+1 have landed
     __syncthreads();
   }
@@ -668,8 +685,10 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
 // iteration ahead, so that the only LDS round trip on the way from one
 // barrier to the next is the one for the P / C^T fragments and the k_r to
 // rotate.
+template <class SegEnd>
 __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
-                                             f32x4_t (&o)[kSplitGroups][kSplitNb]) {
+                                             f32x4_t (&o)[kSplitGroups][kSplitNb], uint32_t seg_tiles,
+                                             SegEnd&& seg_end) {
   const uint32_t lane = threadIdx.x & 63, j = wave_id() - kSplitGroups, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
@@ -755,6 +774,15 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
     }
     slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);
     if (rot && !table) slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d_rot, cd);
+    if constexpr (B) {
+      if (seg_tiles && (t % seg_tiles == 0 || t == nt)) {  // tile t-1 closed a segment
+        seg_end((t - 1) / seg_tiles, o);
+#pragma unroll
+        for (int g = 0; g < kSplitGroups; ++g)
+#pragma unroll
+          for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
     __syncthreads();
   };
 

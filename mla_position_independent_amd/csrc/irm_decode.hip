@@ -25,14 +25,19 @@ struct DecodeArgs {
   float* ws_acc;  // [n_seq][n_splits][n_heads][512], unnormalised
   float* ws_ml;   // [n_seq][n_splits][n_heads][2]: base-2 max, sum
   uint32_t n_seq, n_heads, n_groups, n_splits;
+  uint32_t splits_per_wg;  // shared-tile kernel: consecutive splits per workgroup (divides n_splits)
   float scale_log2;
   InvFreq f;
 };
 
 // Rows [r0, r1) of the split sp of a sequence with N rows: splits are whole
 // multiples of 64 rows so that every wave range and tile is aligned.
+__device__ __forceinline__ uint32_t split_len(uint32_t N, uint32_t n_splits) {
+  return ((N + n_splits - 1) / n_splits + 63) / 64 * 64;
+}
+
 __device__ __forceinline__ void split_rows(uint32_t N, uint32_t n_splits, uint32_t sp, uint32_t& r0, uint32_t& r1) {
-  const uint32_t per = ((N + n_splits - 1) / n_splits + 63) / 64 * 64;
+  const uint32_t per = split_len(N, n_splits);
   r0 = min(N, sp * per);
   r1 = min(N, r0 + per);
 }
@@ -199,45 +204,59 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
 // ---------------------------------------------------------------------------
 // split-KV decode, pass 1, four 16-head groups per workgroup: shared tiles
 //
-// Workgroup = (sequence, split, 64-head block) of eight waves.  Scoring
-// wave s holds head group 4 blk + s; accumulating wave j copies and rotates
-// one 8-row slice of every 32-row tile and sums columns 128 j .. 128 j + 127
-// of all four groups (score_stream / value_stream), so the KV is copied once
-// per 64 heads instead of once per 16.  Partial states go straight to the
-// workspace: O from the accumulating waves, (m, l) from the scoring waves.
+// Workgroup = (sequence, run of U consecutive splits, 64-head block) of eight
+// waves.  Scoring wave s holds head group 4 blk + s; accumulating wave j sums
+// columns 128 j .. 128 j + 127 of all four groups (score_stream /
+// value_stream), so the KV is copied once per 64 heads instead of once per
+// 16.  The U splits are contiguous rows, streamed as one run of tiles with a
+// segment per split (splits are whole multiples of 64 rows, so segments
+// start on tile boundaries), which keeps the copy pipeline full across split
+// boundaries and pays the workgroup's start-up once per run.  Each segment's
+// partial state goes straight to the workspace: O from the accumulating
+// waves, (m, l) from the scoring waves; splits of the run that hold no rows
+// get the empty state (O = 0, m = -inf, l = 0).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) SplitSmem sm;
 
   const uint32_t n_blk = a.n_groups / kSplitGroups;
+  const uint32_t U = a.splits_per_wg, n_runs = a.n_splits / U;
   const uint32_t x = blockIdx.x, xcd = x & 7, slot = x >> 3;
   const uint32_t hb = slot % n_blk;
-  const uint32_t bs = (slot / n_blk) * 8 + xcd;
-  if (bs >= a.n_seq * a.n_splits) return;
-  const uint32_t b = bs / a.n_splits, sp = bs % a.n_splits;
+  const uint32_t br = (slot / n_blk) * 8 + xcd;
+  if (br >= a.n_seq * n_runs) return;
+  const uint32_t b = br / n_runs, sp0 = (br % n_runs) * U;
 
-  const uint32_t base = a.seq_base[b];
-  uint32_t r0, r1;
-  split_rows(a.seq_base[b + 1] - base, a.n_splits, sp, r0, r1);
+  const uint32_t base = a.seq_base[b], N = a.seq_base[b + 1] - base;
+  const uint32_t per = split_len(N, a.n_splits);
+  const uint32_t r0 = min(N, sp0 * per), r1 = min(N, r0 + U * per);
+  const uint32_t seg_tiles = per / kTileRows > 0 ? per / kTileRows : 1;
+  const uint32_t nt = (r1 - r0 + kTileRows - 1) / kTileRows;
+  const uint32_t n_seg = (nt + seg_tiles - 1) / seg_tiles;  // splits of the run that hold rows
 
   const uint32_t lane = threadIdx.x & 63, w = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t g0 = hb * kSplitGroups;  // first head group of the block
-  const size_t pbase = ((size_t)b * a.n_splits + sp) * a.n_heads + g0 * 16;
+  auto pbase = [&](uint32_t k) { return ((size_t)b * a.n_splits + sp0 + k) * a.n_heads + g0 * 16; };
   fill_omega(sm.s.omega, a.f);
 
   if (w < kSplitGroups) {  // scoring wave: head group g0 + w
     bf16x8_t qb[18];
     load_q<false>(a.q_lat, a.q_rope, b, a.n_heads, (g0 + w) * 16 + hr, qb);
     float m = -INFINITY, l = 0.f;
+    auto put_ml = [&](uint32_t k, float mk, float lk) {
+      lk += __shfl_xor(lk, 16);
+      lk += __shfl_xor(lk, 32);
+      if (hq == 0) {
+        float* d = a.ws_ml + (pbase(k) + 16 * w + hr) * 2;
+        d[0] = mk;
+        d[1] = (mk == -INFINITY) ? 0.f : lk;
+      }
+    };
     __syncthreads();
     score_stream(a.ra, sm, r1 - r0, a.scale_log2,
-                 [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l);
-    split_publish(sm, m, l);
-    if (hq == 0) {
-      const float mg = sm.ml[w][hr][0];
-      a.ws_ml[(pbase + 16 * w + hr) * 2 + 0] = mg;
-      a.ws_ml[(pbase + 16 * w + hr) * 2 + 1] = (mg == -INFINITY) ? 0.f : sm.ml[w][hr][1];
-    }
+                 [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l, seg_tiles,
+                 put_ml);
+    for (uint32_t k = n_seg; k < U; ++k) put_ml(k, -INFINITY, 0.f);
     return;
   }
 
@@ -248,16 +267,18 @@ __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeAr
   for (int g = 0; g < kSplitGroups; ++g)
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto put_o = [&](uint32_t k, const f32x4_t(&ok)[kSplitGroups][kSplitNb]) {
+#pragma unroll
+    for (int g = 0; g < kSplitGroups; ++g) {
+      float* dst = a.ws_acc + (pbase(k) + 16 * g + hr) * IRM_D_LATENT + kSplitCols * j + 4 * hq;
+#pragma unroll
+      for (int nb = 0; nb < kSplitNb; ++nb)
+        *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(ok[g][nb][0], ok[g][nb][1], ok[g][nb][2], ok[g][nb][3]);
+    }
+  };
   __syncthreads();
-  value_stream(a.ra, sm, base + r0, r1 - r0, o);
-  split_publish_wait();
-#pragma unroll
-  for (int g = 0; g < kSplitGroups; ++g) {
-    float* dst = a.ws_acc + (pbase + 16 * g + hr) * IRM_D_LATENT + kSplitCols * j + 4 * hq;
-#pragma unroll
-    for (int nb = 0; nb < kSplitNb; ++nb)
-      *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[g][nb][0], o[g][nb][1], o[g][nb][2], o[g][nb][3]);
-  }
+  value_stream(a.ra, sm, base + r0, r1 - r0, o, seg_tiles, put_o);
+  for (uint32_t k = n_seg; k < U; ++k) put_o(k, o);  // o is zero here
 }
 
 // ---------------------------------------------------------------------------
@@ -339,6 +360,31 @@ uint32_t decode_default_splits(const irm_table* t, uint32_t n_groups) {
   return s;
 }
 
+// Compute units of the current device (cached per thread and device).
+static uint32_t cu_count() {
+  static thread_local int dev_cached = -1;
+  static thread_local uint32_t n_cached = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return n_cached;
+  if (dev != dev_cached) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      n_cached = (uint32_t)n;
+    dev_cached = dev;
+  }
+  return n_cached;
+}
+
+// Consecutive splits per workgroup of the shared-tile kernel: the largest
+// divisor of n_splits that still leaves a workgroup for every compute unit.
+static uint32_t splits_per_workgroup(uint32_t n_seq, uint32_t n_splits, uint32_t n_blk) {
+  const uint64_t cus = cu_count();
+  uint32_t best = 1;
+  for (uint32_t u = 2; u <= n_splits; ++u)
+    if (n_splits % u == 0 && (uint64_t)n_seq * (n_splits / u) * n_blk >= cus) best = u;
+  return best;
+}
+
 irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_rope, const void* pool,
                          uint64_t pool_rows, uint32_t n_heads, uint32_t n_splits, float scale, void* out,
                          float* lse, float* ws_acc, float* ws_ml, hipStream_t s) {
@@ -357,7 +403,8 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
   a.scale_log2 = scale * kLog2e;
   for (int i = 0; i < (int)kPairs; ++i) a.f.w[i] = t->inv_freq[i];
   const bool shared = G % kSplitGroups == 0;
-  const uint64_t bs = (uint64_t)t->n_seq * n_splits;
+  a.splits_per_wg = shared ? splits_per_workgroup(t->n_seq, n_splits, G / kSplitGroups) : 1;
+  const uint64_t bs = (uint64_t)t->n_seq * (n_splits / a.splits_per_wg);
   const uint64_t grid = (bs + 7) / 8 * 8 * (shared ? G / kSplitGroups : G);
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");
   if (shared)

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
                    const int64_t last = lim - (int64_t)t * kTileRows;
                    return last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last);
                  },
-                 qb, m, l);
+                 qb, m, l, 0, [](uint32_t, float, float) {});
     split_publish(sm, m, l);
     if (a.lse && qi < a.n_q && hq == 0)
       a.lse[(size_t)qi * a.n_heads + head] = (sm.ml[w][hr][0] + log2f(sm.ml[w][hr][1])) * kLn2;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  value_stream(a.ra, sm, a.seq_base[0], rows, o);
+  value_stream(a.ra, sm, a.seq_base[0], rows, o, 0, [](uint32_t, const f32x4_t(&)[kSplitGroups][kSplitNb]) {});
   split_publish_wait();
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g) {

@@ -263,6 +263,22 @@ def test_decode_rescale_paths(heads):
     assert np.max(np.abs(l - l_ref)) <= 4.0 * LSE_TOL
 
 
+@pytest.mark.parametrize("heads,n_seq", [(64, 40), (128, 20)])
+def test_decode_split_runs(heads, n_seq):
+    """Enough (sequence, split) pairs that one workgroup of the 64-head kernel
+    streams several consecutive splits (two on a 256-CU part) as segments of
+    one run; ragged lengths leave partial and empty splits inside the runs."""
+    rng = np.random.default_rng(34)
+    lens = [int(x) for x in rng.integers(1, 1200, size=n_seq - 1)] + [2048]
+    w = random_table(34, lens, heads=heads, p_hit=0.8)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    o, l = _gpu_decode(w, 16)
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= LSE_TOL
+    for b in range(w.n_seq):
+        assert rel_l2(o[b], o_ref[b]) <= ATTN_TOL, b
+
+
 def test_decode_split_invariance_and_determinism():
     w = random_table(11, [4096, 2500], heads=16)
     o_ref, _ = _oracle_decode(w, range(w.n_seq))
