@@ -222,6 +222,94 @@ irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_rope, int32_
                                 uint64_t pool_rows, uint32_t n_heads, float scale,
                                 void* out, float* lse, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Host chunk-table producer (no HIP call; usable without a GPU).
+ *
+ * The serve path of the pages splits a request's unmatched tail by
+ * content-defined chunking (CDC), fingerprints every chunk with xxHash64 and
+ * looks it up in a content registry: a hit at target position p is reused
+ * with delta = p - p_src, a miss is prefilled and inserted as
+ * (c_KV, k_r_base, p), and a segment starting below position 32 is always
+ * prefilled (gentlecold.top article, section 5 pseudocode).  The chunker is a
+ * rolling Gear hash over a 64-token window that cuts where its low 7 bits
+ * meet the mask, chunks of about 128 tokens clamped to [32, 512]
+ * (gentlecold.top section 6; gist.science summary, section 2.2).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * CDC parameters.  The Gear state is 64 bits: h = (h << 1) + gear(token)
+ * mod 2^64, starting at 0 at the first token and rolling on across chunk
+ * boundaries; gear(t) is the splitmix64 output for the state
+ * seed + t * 0x9E3779B97F4A7C15 (the pages give no table; this one is ours).
+ * A chunk ends after token i when it holds at least min_len tokens and
+ * h & (2^mask_bits - 1) == 0, or when it holds max_len tokens; the last chunk
+ * takes what remains.
+ */
+typedef struct irm_cdc_params {
+  uint64_t seed;
+  uint32_t mask_bits; /* 1..63 */
+  uint32_t min_len;   /* >= 1 */
+  uint32_t max_len;   /* >= min_len */
+} irm_cdc_params;
+
+/* The values the pages fix: mask_bits 7, [min_len, max_len] = [32, 512]; seed 0. */
+irm_status irm_cdc_params_default(irm_cdc_params* p);
+
+/*
+ * Chunk lengths of a token stream.
+ *   host tokens[n] (token ids); host out lens[max_chunks]; *n_chunks receives
+ *   the number of chunks (also when it exceeds max_chunks: ERANGE, nothing
+ *   written).  EINVAL for bad parameters or NULL pointers.
+ */
+irm_status irm_cdc_split(const irm_cdc_params* p, const int32_t* tokens, uint64_t n, uint32_t* lens,
+                         uint64_t max_chunks, uint64_t* n_chunks);
+
+/* xxHash64 (per its specification) of host data[bytes] with the given seed. */
+irm_status irm_xxh64(const void* data, uint64_t bytes, uint64_t seed, uint64_t* out);
+
+/*
+ * Content registry: fingerprint -> (pool_row, len, p_src), plus the counter
+ * that allocates pool rows for freshly prefilled segments, starting at
+ * first_free_row.  Host memory owned by the library; free with
+ * irm_registry_destroy.  Not thread-safe: one call at a time per registry.
+ */
+typedef struct irm_registry irm_registry;
+irm_status irm_registry_create(uint64_t first_free_row, irm_registry** out);
+irm_status irm_registry_destroy(irm_registry* r);
+irm_status irm_registry_info(const irm_registry* r, uint64_t* n_entries, uint64_t* next_free_row);
+
+/*
+ * Turn a batch of requests into one chunk table (the input of
+ * irm_table_create).
+ *   host tokens: the requests' token ids back to back; host tok_first[n_req+1]:
+ *   request q owns tokens [tok_first[q], tok_first[q+1]) (tok_first[0] == 0,
+ *   nondecreasing, each request < 2^31 tokens).
+ *   host prefix_len[n_req], prefix_row[n_req] (either may be NULL = 0): the
+ *   exact-prefix match of the request (a standard prefix cache, outside the
+ *   method), already in the pool from row prefix_row; it is emitted as a
+ *   fresh entry for its first min(prefix_len, 32) rows and an exact-prefix
+ *   entry (delta 0) for the rest.
+ *   The tail after the prefix is CDC-split with *p; each chunk at target
+ *   position pos: pos < 32 -> fresh entry on newly allocated rows, not
+ *   registered; fingerprint hit with the same length -> registry entry
+ *   (pool_row, len, p_src) placed at pos; otherwise fresh entry on newly
+ *   allocated rows, registered with p_src = pos (a stored entry of another
+ *   length is replaced).  Fingerprint = xxHash64, seed 0, of the chunk's ids
+ *   as 4-byte little-endian integers.  Requests are processed in order, so a
+ *   chunk inserted by request q is a hit for request q+1.
+ *   CDC and fingerprints run on n_threads host threads (0 = all cores).
+ *   host out chunks[max_chunks], fingerprints[max_chunks] (optional; 0 for
+ *   prefix entries), seq_first[n_req + 1]; *n_chunks = entries.  Every fresh
+ *   entry's rows are the caller's to prefill at p_tgt.
+ *   ERANGE with *n_chunks = the needed count, and the registry unchanged, if
+ *   max_chunks is too small or the allocation counter would pass 2^32 rows.
+ */
+irm_status irm_registry_assemble(irm_registry* r, const irm_cdc_params* p, const int32_t* tokens,
+                                 const uint64_t* tok_first, uint32_t n_req, const uint32_t* prefix_len,
+                                 const uint32_t* prefix_row, uint32_t n_threads, irm_chunk* chunks,
+                                 uint64_t* fingerprints, uint32_t max_chunks, uint32_t* seq_first,
+                                 uint32_t* n_chunks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,15 @@ EXPORTS = (
     "irm_table_set_rope",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
     "irm_mla_decode", "irm_mla_prefill_tail",
+    "irm_cdc_params_default", "irm_cdc_split", "irm_xxh64", "irm_registry_create",
+    "irm_registry_destroy", "irm_registry_info", "irm_registry_assemble",
 )
+
+
+class CdcParams(ctypes.Structure):
+    """irm_cdc_params: Gear seed, mask bits, chunk length bounds."""
+    _fields_ = [("seed", ctypes.c_uint64), ("mask_bits", ctypes.c_uint32), ("min_len", ctypes.c_uint32),
+                ("max_len", ctypes.c_uint32)]
 
 
 class IrmError(RuntimeError):
@@ -76,6 +84,14 @@ def lib() -> ctypes.CDLL:
         "irm_mla_decode_workspace": (ctypes.c_int, [vp, u32, u32, P(sz)]),
         "irm_mla_decode": (ctypes.c_int, [vp, vp, vp, vp, u64, u32, u32, ctypes.c_float, vp, vp, vp, sz, vp]),
         "irm_mla_prefill_tail": (ctypes.c_int, [vp, vp, i32, u32, vp, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
+        "irm_cdc_params_default": (ctypes.c_int, [P(CdcParams)]),
+        "irm_cdc_split": (ctypes.c_int, [P(CdcParams), vp, u64, vp, u64, P(u64)]),
+        "irm_xxh64": (ctypes.c_int, [vp, u64, u64, P(u64)]),
+        "irm_registry_create": (ctypes.c_int, [u64, P(vp)]),
+        "irm_registry_destroy": (ctypes.c_int, [vp]),
+        "irm_registry_info": (ctypes.c_int, [vp, P(u64), P(u64)]),
+        "irm_registry_assemble": (ctypes.c_int, [vp, P(CdcParams), vp, vp, u32, vp, vp, u32, vp, vp, u32, vp,
+                                                 P(u32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -275,3 +291,88 @@ def from_device_bf16(t) -> np.ndarray:
     """torch bf16 CUDA tensor -> uint16 bit patterns (host)."""
     import torch
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- chunk-table producer (host)
+def cdc_params(seed: int = 0, mask_bits: Optional[int] = None, min_len: Optional[int] = None,
+               max_len: Optional[int] = None) -> CdcParams:
+    """CDC parameters: the library defaults (mask 7 bits, [32, 512]) unless given."""
+    p = CdcParams()
+    _check(lib().irm_cdc_params_default(ctypes.byref(p)), "irm_cdc_params_default")
+    p.seed = int(seed) & (2**64 - 1)
+    if mask_bits is not None:
+        p.mask_bits = mask_bits
+    if min_len is not None:
+        p.min_len = min_len
+    if max_len is not None:
+        p.max_len = max_len
+    return p
+
+
+def cdc_split(tokens, params: Optional[CdcParams] = None) -> np.ndarray:
+    """Chunk lengths (uint32) of a token stream."""
+    toks = np.ascontiguousarray(tokens, dtype=np.int32)
+    p = cdc_params() if params is None else params
+    n = ctypes.c_uint64()
+    cap = max(1, toks.size // max(1, p.min_len) + 1)
+    lens = np.zeros(cap, dtype=np.uint32)
+    _check(lib().irm_cdc_split(ctypes.byref(p), toks.ctypes.data, toks.size, lens.ctypes.data, cap,
+                               ctypes.byref(n)), "irm_cdc_split")
+    return lens[:n.value].copy()
+
+
+def xxh64(data: bytes, seed: int = 0) -> int:
+    out = ctypes.c_uint64()
+    buf = ctypes.create_string_buffer(bytes(data), max(1, len(data)))
+    _check(lib().irm_xxh64(buf, len(data), int(seed) & (2**64 - 1), ctypes.byref(out)), "irm_xxh64")
+    return out.value
+
+
+class Registry:
+    """Content registry (fingerprint -> pool_row, len, p_src) with its
+    fresh-row allocation counter, owned by the library."""
+
+    def __init__(self, first_free_row: int = 0):
+        h = ctypes.c_void_p()
+        _check(lib().irm_registry_create(int(first_free_row), ctypes.byref(h)), "irm_registry_create")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.irm_registry_destroy(h)
+            self._h = None
+
+    def info(self) -> Tuple[int, int]:
+        n, nxt = ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib().irm_registry_info(self._h, ctypes.byref(n), ctypes.byref(nxt)), "irm_registry_info")
+        return n.value, nxt.value
+
+    def assemble(self, requests, prefix_len=None, prefix_row=None, params: Optional[CdcParams] = None,
+                 n_threads: int = 0):
+        """requests: sequence of int32 token arrays.  Returns (chunks
+        [CHUNK_DTYPE], seq_first [uint32, n_req + 1], fingerprints [uint64])."""
+        reqs = [np.ascontiguousarray(r, dtype=np.int32) for r in requests]
+        n_req = len(reqs)
+        tok_first = np.zeros(n_req + 1, dtype=np.uint64)
+        tok_first[1:] = np.cumsum([r.size for r in reqs]) if n_req else []
+        toks = np.concatenate(reqs) if n_req and tok_first[-1] else np.zeros(1, dtype=np.int32)
+        pl = None if prefix_len is None else np.ascontiguousarray(prefix_len, dtype=np.uint32)
+        pr = None if prefix_row is None else np.ascontiguousarray(prefix_row, dtype=np.uint32)
+        p = cdc_params() if params is None else params
+        seq_first = np.zeros(n_req + 1, dtype=np.uint32)
+        n = ctypes.c_uint32()
+        cap = 16
+        while True:
+            chunks = np.zeros(cap, dtype=CHUNK_DTYPE)
+            prints = np.zeros(cap, dtype=np.uint64)
+            st = lib().irm_registry_assemble(
+                self._h, ctypes.byref(p), toks.ctypes.data, tok_first.ctypes.data, n_req,
+                None if pl is None else pl.ctypes.data, None if pr is None else pr.ctypes.data, int(n_threads),
+                chunks.ctypes.data, prints.ctypes.data, cap, seq_first.ctypes.data, ctypes.byref(n))
+            if st == 2 and n.value > cap:      # ERANGE: grow to the count the library reports
+                cap = n.value
+                continue
+            _check(st, "irm_registry_assemble")
+            return chunks[:n.value].copy(), seq_first, prints[:n.value].copy()
+
