@@ -10,8 +10,11 @@ already resident in HBM.  ``value`` is assembled KV tokens per second.
 Further legs time MLA decode with rotation on load (batch 64 x 8192 tokens
 x 16 heads; batch 32 x 32768 x 128 heads with 16 splits) and the chunked
 tail-prefill (4096 queries over 65536 rows, 16 heads) with the same
-methodology, each with its own roofline.  The CPU oracle is timed on a
-bounded sample of the rotate-gather batch as ``cpu_baseline``.
+methodology, each with its own roofline, and the host chunk-table producer
+(content-defined chunking, fingerprints and registry lookups for 64 requests
+x 32768 tokens against a warm registry; host work, no GPU).  The CPU oracle
+is timed on a bounded sample of the rotate-gather batch as ``cpu_baseline``
+(and of the producer batch inside the producer leg).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
 """
@@ -242,6 +245,49 @@ def leg_prefill(args, irm, torch, synth):
     }
 
 
+def leg_producer(args, irm, synth, oracle_seconds: float):
+    """Host chunk-table producer: irm_registry_assemble on 64 requests x 32768
+    tokens (shared documents at shifted offsets, 80% of segments), the
+    registry warmed by one earlier batch of the same mix."""
+    import numpy as np
+    warm = synth.token_requests(seed=1106)
+    reqs = synth.token_requests(seed=1006)
+    n_tok = int(sum(r.size for r in reqs))
+    threads = min(16, os.cpu_count() or 1)  # the host share of one GPU
+    times = []
+    for k in range(args.warmup + args.steps):
+        reg = irm.Registry(0)
+        reg.assemble(warm, n_threads=threads)
+        t0 = time.perf_counter()
+        chunks, seq_first, _ = reg.assemble(reqs, n_threads=threads)
+        dt = time.perf_counter() - t0
+        if k >= args.warmup:
+            times.append(dt)
+    ms = 1e3 * float(np.median(times))
+    hit_tok = float(chunks["len"][chunks["flags"] == 0].sum()) / n_tok
+    log(f"producer: {ms:.3f} ms per batch, {n_tok / (ms * 1e-3):.4g} tokens/s on {threads} threads, "
+        f"{hit_tok:.1%} of tokens from the registry")
+    res = {"workload": "token_requests_64x32768", "ms_per_call": round(ms, 4), "tokens": n_tok,
+           "value": round(n_tok / (ms * 1e-3), 1), "unit": "tokens/s (host)", "threads": threads,
+           "entries": int(chunks.shape[0]), "registry_token_fraction": round(hit_tok, 4)}
+    if oracle_seconds > 0:
+        from oracle import irm_producer
+        oreg = irm_producer.Registry(0)
+        for r in warm[:4]:
+            oreg.assemble(list(r))
+        done, spent = 0, 0.0
+        for r in reqs:
+            t0 = time.perf_counter()
+            oreg.assemble(list(r))
+            spent += time.perf_counter() - t0
+            done += r.size
+            if spent >= oracle_seconds:
+                break
+        res["cpu_baseline"] = {"value": round(done / spent, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} tokens of the batch, {spent:.1f} s single-threaded Python"}
+    return res
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle, single-threaded, on the first requests of the rotate-gather
     batch until ``seconds`` of CPU work have been spent (at least one)."""
@@ -273,7 +319,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="gather,decode,long_decode,prefill",
+    ap.add_argument("--legs", default="gather,decode,long_decode,prefill,producer",
                     help="comma list; without gather only the named legs run (profiling, no JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -325,6 +371,8 @@ def main():
                 leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)
             elif name == "prefill":
                 leg_prefill(args, irm, torch, synth)
+            elif name == "producer":
+                leg_producer(args, irm, synth, 0.0)
         return
     g = leg_gather(args, irm, torch, synth)
     extra = {}
@@ -334,6 +382,8 @@ def main():
         extra["long_decode"] = leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)
     if "prefill" in legs:
         extra["prefill"] = leg_prefill(args, irm, torch, synth)
+    if "producer" in legs:
+        extra["producer"] = leg_producer(args, irm, synth, 0.0 if args.no_cpu_baseline else 3.0)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -21,5 +21,6 @@ from .workloads import (  # noqa: F401
     batched_decode,
     long_decode,
     tail_prefill,
+    token_requests,
     manifest,
 )

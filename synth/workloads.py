@@ -326,6 +326,37 @@ def random_table(seed: int, seq_lens: List[int], heads: int = 16, p_hit: float =
                     q_lat=q_lat, q_rope=q_rope, kind=kind)
 
 
+def token_requests(seed: int = 1006, n_req: int = 64, req_len: int = 32768, n_docs: int = 256,
+                   doc_len: Tuple[int, int] = (1024, 8192), p_doc: float = 0.8,
+                   fresh_len: Tuple[int, int] = (64, 2048), vocab: int = 128000,
+                   library_seed: int = 2006) -> List[np.ndarray]:
+    """Token streams for the chunk-table producer: each request concatenates
+    segments until ``req_len`` tokens, a whole shared document (drawn from a
+    library of ``n_docs`` documents with lengths uniform in ``doc_len``) with
+    probability ``p_doc``, else fresh tokens (lengths uniform in
+    ``fresh_len``); the last segment is truncated.  Token ids are uniform in
+    [0, vocab).  The library depends only on ``library_seed``, so batches with
+    different ``seed`` share documents at shifted offsets (the agentic reuse
+    pattern the pages describe)."""
+    lib_rng = np.random.default_rng(library_seed)
+    docs = [lib_rng.integers(0, vocab, size=int(lib_rng.integers(doc_len[0], doc_len[1] + 1)), dtype=np.int32)
+            for _ in range(n_docs)]
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_req):
+        parts, n = [], 0
+        while n < req_len:
+            if rng.random() < p_doc:
+                seg = docs[int(rng.integers(0, n_docs))]
+            else:
+                seg = rng.integers(0, vocab, size=int(rng.integers(fresh_len[0], fresh_len[1] + 1)), dtype=np.int32)
+            seg = seg[:req_len - n]
+            parts.append(seg)
+            n += seg.size
+        out.append(np.concatenate(parts).astype(np.int32))
+    return out
+
+
 WORKLOADS = {
     "tiny_decode": tiny_decode,
     "rotate_gather": rotate_gather_batch,
