@@ -711,12 +711,15 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
     constexpr bool B = decltype(kB)::value;
     unsigned char* nx = stage(t + 2);
     unsigned char* sr = stage(t + 1) + kTileKr;
-    const bool rot = t + 1 < nt;
+    // Tile t+1 needs turning unless every row of the slice has delta 0
+    // (exact-prefix and fresh rows, or a slice past the end).
+    const bool rot = t + 1 < nt && __any(d1 != 0);
     const bool table = rot && slice_trig_ready(ws, sm.s.omega, d1, cd);
     // Tile t+1 has landed: after its copies only the row map of tile t+3
     // went out (t >= 1); at t = 0 nothing did.
     wait_dma_but<B ? 1 : 0>();
-    const SliceRot rt = slice_rot_load(ws, sr, row0, d1, cd);
+    SliceRot rt;
+    if (table) rt = slice_rot_load(ws, sr, row0, d1, cd);
     const int32_t d_rot = d1;
     copy_kr(ra, cp, nx + kTileKr, row0);
     auto mid = [&]() {
