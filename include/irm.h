@@ -222,6 +222,22 @@ irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_rope, int32_
                                 uint64_t pool_rows, uint32_t n_heads, float scale,
                                 void* out, float* lse, void* stream);
 
+/*
+ * Chunked tail-prefill over an assembled cache (the output of
+ * irm_rotate_gather for one sequence): the same causal absorbed MLA attention
+ * as irm_mla_prefill_tail, with row r of kv at position r and no rotation
+ * left to apply.  Assembling once and attending over the result serves every
+ * query block from the same rotated rows, where irm_mla_prefill_tail turns
+ * each row again for every block of four queries.
+ *   device kv bf16 [kv_rows][576] (16-byte aligned); queries, out and lse as
+ *   in irm_mla_prefill_tail; query i attends rows t <= q_pos0 + i.
+ *   0 <= q_pos0, 1 <= n_q, q_pos0 + n_q <= kv_rows (ERANGE); kv_rows <= 2^32
+ *   and n_heads a multiple of 16, <= 128 (EUNSUPPORTED).
+ */
+irm_status irm_mla_prefill_assembled(const void* q_latent, const void* q_rope, int32_t q_pos0,
+                                     uint32_t n_q, const void* kv, uint64_t kv_rows, uint32_t n_heads,
+                                     float scale, void* out, float* lse, void* stream);
+
 /* ------------------------------------------------------------------------
  * Host chunk-table producer (no HIP call; usable without a GPU).
  *

@@ -36,7 +36,7 @@ EXPORTS = (
     "irm_table_info", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
     "irm_table_set_rope",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
-    "irm_mla_decode", "irm_mla_prefill_tail",
+    "irm_mla_decode", "irm_mla_prefill_tail", "irm_mla_prefill_assembled",
     "irm_cdc_params_default", "irm_cdc_split", "irm_xxh64", "irm_registry_create",
     "irm_registry_destroy", "irm_registry_info", "irm_registry_assemble",
 )
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "irm_mla_decode_workspace": (ctypes.c_int, [vp, u32, u32, P(sz)]),
         "irm_mla_decode": (ctypes.c_int, [vp, vp, vp, vp, u64, u32, u32, ctypes.c_float, vp, vp, vp, sz, vp]),
         "irm_mla_prefill_tail": (ctypes.c_int, [vp, vp, i32, u32, vp, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
+        "irm_mla_prefill_assembled": (ctypes.c_int, [vp, vp, i32, u32, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
         "irm_cdc_params_default": (ctypes.c_int, [P(CdcParams)]),
         "irm_cdc_split": (ctypes.c_int, [P(CdcParams), vp, u64, vp, u64, P(u64)]),
         "irm_xxh64": (ctypes.c_int, [vp, u64, u64, P(u64)]),
@@ -278,6 +279,26 @@ def mla_prefill_tail(q_lat, q_rope, q_pos0: int, table: Table, pool, scale: floa
     _check(lib().irm_mla_prefill_tail(_ptr(q_lat), _ptr(q_rope), int(q_pos0), nq, table.handle, _ptr(pool),
                                       pool.shape[0], H, float(scale), _ptr(out), _ptr(lse),
                                       _stream(stream)), "irm_mla_prefill_tail")
+    return (out, lse) if want_lse else out
+
+
+def mla_prefill_assembled(q_lat, q_rope, q_pos0: int, kv, scale: float = DEFAULT_SCALE, out=None,
+                          want_lse: bool = False, stream=None):
+    """Causal tail-prefill over an assembled cache kv (bf16 [rows][576], row r
+    at position r, e.g. the output of rotate_gather for one sequence)."""
+    import torch
+    _bf16_2d(kv, ROW, "kv")
+    _bf16_2d(q_lat, D_LATENT, "q_lat")
+    _bf16_2d(q_rope, D_ROPE, "q_rope")
+    nq, H = q_lat.shape[0], q_lat.shape[1]
+    if tuple(q_rope.shape) != (nq, H, D_ROPE):
+        raise ValueError("q_rope must be [n_q][H][64]")
+    if out is None:
+        out = torch.empty((nq, H, D_LATENT), dtype=torch.bfloat16, device=kv.device)
+    lse = torch.empty((nq, H), dtype=torch.float32, device=kv.device) if want_lse else None
+    _check(lib().irm_mla_prefill_assembled(_ptr(q_lat), _ptr(q_rope), int(q_pos0), nq, _ptr(kv), kv.shape[0], H,
+                                           float(scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "irm_mla_prefill_assembled")
     return (out, lse) if want_lse else out
 
 

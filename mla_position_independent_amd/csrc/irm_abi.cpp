@@ -186,3 +186,21 @@ extern "C" irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_r
   return irm::launch_prefill(t, q_latent, q_rope, q_pos0, n_q, pool, pool_rows, n_heads, scale, out, lse,
                              static_cast<hipStream_t>(stream));
 }
+
+extern "C" irm_status irm_mla_prefill_assembled(const void* q_latent, const void* q_rope, int32_t q_pos0,
+                                                uint32_t n_q, const void* kv, uint64_t kv_rows, uint32_t n_heads,
+                                                float scale, void* out, float* lse, void* stream) {
+  static const char* fn = "irm_mla_prefill_assembled";
+  irm_status st = check_heads(n_heads, fn);
+  if (st != IRM_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(IRM_EINVAL, std::string(fn) + ": scale must be finite and > 0");
+  if (kv_rows > 0x100000000ull) return fail(IRM_EUNSUPPORTED, std::string(fn) + ": at most 2^32 cache rows");
+  if (q_pos0 < 0 || n_q == 0 || (uint64_t)q_pos0 + n_q > kv_rows)
+    return fail(IRM_ERANGE, std::string(fn) + ": queries must satisfy 0 <= q_pos0, 1 <= n_q, q_pos0 + n_q <= kv_rows");
+  if (!kv || !aligned16(kv)) return fail(IRM_EINVAL, std::string(fn) + ": kv must be non-NULL and 16-byte aligned");
+  if (!q_latent || !q_rope || !out || !aligned16(q_latent) || !aligned16(q_rope) || !aligned16(out))
+    return fail(IRM_EINVAL, std::string(fn) + ": q_latent, q_rope and out must be non-NULL and 16-byte aligned");
+  if ((st = check_device()) != IRM_OK) return st;
+  return irm::launch_prefill_assembled(q_latent, q_rope, q_pos0, n_q, kv, kv_rows, n_heads, scale, out, lse,
+                                       static_cast<hipStream_t>(stream));
+}

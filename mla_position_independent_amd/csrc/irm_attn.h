@@ -587,6 +587,10 @@ __device__ __forceinline__ void slice_rot_store(unsigned char* kr, uint32_t row0
 // so every iteration issues the same copies per wave and the waits count
 // them.  Barriers per call: nt + 2 on both sides, none when nt = 0.
 //
+// Flat mode (kFlat): the rows are an assembled cache, row g of the stream is
+// row g of the buffer and every delta is 0, so no row maps are copied and
+// nothing is rotated.
+//
 // Segments: with seg_tiles > 0 the rows form consecutive segments of
 // seg_tiles tiles (the last one may be shorter), each with its own softmax
 // state.  The scorers hand (m, l) of a segment to seg_end(k, m, l) after its
@@ -608,10 +612,10 @@ __device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirs
 // accumulator of that slice copies the rest, its k_r and row maps), from the
 // row-map records the accumulator published one barrier earlier, and waits
 // for them before the barrier that ends iteration t+1.
-template <class Last, class SegEnd>
-__device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t n, float c, Last&& last,
-                                             const bf16x8_t (&qb)[18], float& m, float& l, uint32_t seg_tiles,
-                                             SegEnd&& seg_end) {
+template <bool kFlat, class Last, class SegEnd>
+__device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
+                                             float c, Last&& last, const bf16x8_t (&qb)[18], float& m, float& l,
+                                             uint32_t seg_tiles, SegEnd&& seg_end) {
   const uint32_t lane = threadIdx.x & 63, s = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
@@ -623,7 +627,12 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
     uint32_t src[kScoreRows > 0 ? kScoreRows : 1];
     unsigned char* nx = sm.s.stage[(t + 2) % kStages];
 #pragma unroll
-    for (int k = 0; k < kScoreRows; ++k) src[k] = min(ws.rm[(t + 2) % kTileRm][k].x, ra.pool_last);
+    for (int k = 0; k < kScoreRows; ++k) {
+      if constexpr (kFlat)
+        src[k] = min(g_begin + min(t + 2, nt - 1) * kTileRows + row0 + k, ra.pool_last);
+      else
+        src[k] = min(ws.rm[(t + 2) % kTileRm][k].x, ra.pool_last);
+    }
     const unsigned char* sa = sm.s.stage[t % kStages];
     const unsigned char* rowp = sa + rr * kCkvBytes + ((q ^ (rr & 3)) << 4);
     const unsigned char* base[4];
@@ -685,7 +694,7 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
 // iteration ahead, so that the only LDS round trip on the way from one
 // barrier to the next is the one for the P / C^T fragments and the k_r to
 // rotate.
-template <class SegEnd>
+template <bool kFlat, class SegEnd>
 __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
                                              f32x4_t (&o)[kSplitGroups][kSplitNb], uint32_t seg_tiles,
                                              SegEnd&& seg_end) {
@@ -697,7 +706,26 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
   int32_t cd[2] = {0, 0};
   auto g0 = [&](uint32_t x) { return g_begin + min(x, nt - 1) * kTileRows + row0; };
   auto stage = [&](uint32_t x) { return sm.s.stage[x % kStages]; };
-  auto delta = [&](uint32_t x) { return slice_row_delta<kTileSlice>(ws.rm[x % kTileRm]); };
+  auto delta = [&](uint32_t x) -> int32_t {
+    if constexpr (kFlat)
+      return 0;
+    else
+      return slice_row_delta<kTileSlice>(ws.rm[x % kTileRm]);
+  };
+  // copy sources of tile x: from its row map, or consecutive rows (flat)
+  auto copies_of = [&](uint32_t x) -> SliceCopies {
+    if constexpr (kFlat) {
+      SliceCopies c;
+      const uint32_t r = g0(x);
+#pragma unroll
+      for (int k = 0; k < kTileSlice; ++k) c.src[k] = min(r + k, ra.pool_last);
+      c.ksrc = min(r + (opaque(lane) >> 3), ra.pool_last);
+      return c;
+    } else {
+      return prep_copies(ra, ws.rm[x % kTileRm]);
+    }
+  };
+  constexpr int kRowMaps = kFlat ? 0 : 1;  // row-map copies per iteration
 
   SliceCopies cp;  // copy sources of tile t+2
   int32_t d1;      // delta of this lane's row of tile t+1
@@ -717,7 +745,7 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
     const bool table = rot && slice_trig_ready(ws, sm.s.omega, d1, cd);
     // Tile t+1 has landed: after its copies only the row map of tile t+3
     // went out (t >= 1); at t = 0 nothing did.
-    wait_dma_but<B ? 1 : 0>();
+    wait_dma_but<B ? kRowMaps : 0>();
     SliceRot rt;
     if (table) rt = slice_rot_load(ws, sr, row0, d1, cd);
     const int32_t d_rot = d1;
@@ -726,8 +754,8 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
       if (table) slice_rot_store(sr, row0, rt);
       // This iteration's copies of tile t+2 are out; the row map of tile
       // t+3, issued before them, has landed.
-      wait_dma_but<kTileSlice - kScoreRows + 1>();
-      cp = prep_copies(ra, ws.rm[(t + 3) % kTileRm]);
+      if constexpr (!kFlat) wait_dma_but<kTileSlice - kScoreRows + 1>();
+      cp = copies_of(t + 3);
       d1 = delta(t + 2);
     };
     if constexpr (B) {
@@ -775,7 +803,7 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
       for (int k = kScoreRows; k < kTileSlice; ++k) copy_ckv(ra, cp, k, nx, row0);
       mid();
     }
-    slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);
+    if constexpr (!kFlat) slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);
     if (rot && !table) slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d_rot, cd);
     if constexpr (B) {
       if (seg_tiles && (t % seg_tiles == 0 || t == nt)) {  // tile t-1 closed a segment
@@ -789,15 +817,17 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
     __syncthreads();
   };
 
-  for (uint32_t x = 0; x < 4; ++x) slice_issue_rowmap<kTileSlice>(ra, g0(x), ws.rm[x]);
-  wait_dma_all();
+  if constexpr (!kFlat) {
+    for (uint32_t x = 0; x < 4; ++x) slice_issue_rowmap<kTileSlice>(ra, g0(x), ws.rm[x]);
+    wait_dma_all();
+  }
   for (uint32_t x = 0; x < 2; ++x) {  // copies of tiles 0 and 1 (iterations 0, 1 fetch row maps 4, 5)
-    const SliceCopies c = prep_copies(ra, ws.rm[x]);
+    const SliceCopies c = copies_of(x);
 #pragma unroll
     for (int k = 0; k < kTileSlice; ++k) copy_ckv(ra, c, k, stage(x), row0);
     copy_kr(ra, c, stage(x) + kTileKr, row0);
   }
-  cp = prep_copies(ra, ws.rm[2]);
+  cp = copies_of(2);
   d1 = delta(1);
   wait_dma_but<kTileSlice + 1>();  // tile 0 has landed (tile 1's copies may be outstanding)
   slice_rotate<kTileSlice>(ws, stage(0) + kTileKr, row0, sm.s.omega, delta(0), cd);

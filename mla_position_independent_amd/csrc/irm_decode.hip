@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeAr
       }
     };
     __syncthreads();
-    score_stream(a.ra, sm, r1 - r0, a.scale_log2,
+    score_stream<false>(a.ra, sm, base + r0, r1 - r0, a.scale_log2,
                  [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l, seg_tiles,
                  put_ml);
     for (uint32_t k = n_seg; k < U; ++k) put_ml(k, -INFINITY, 0.f);
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeAr
     }
   };
   __syncthreads();
-  value_stream(a.ra, sm, base + r0, r1 - r0, o, seg_tiles, put_o);
+  value_stream<false>(a.ra, sm, base + r0, r1 - r0, o, seg_tiles, put_o);
   for (uint32_t k = n_seg; k < U; ++k) put_o(k, o);  // o is zero here
 }
 

@@ -30,6 +30,9 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
 irm_status launch_prefill(const irm_table* t, const void* q_lat, const void* q_rope, int32_t q_pos0,
                           uint32_t n_q, const void* pool, uint64_t pool_rows, uint32_t n_heads, float scale,
                           void* out, float* lse, hipStream_t s);
+irm_status launch_prefill_assembled(const void* q_lat, const void* q_rope, int32_t q_pos0, uint32_t n_q,
+                                    const void* kv, uint64_t kv_rows, uint32_t n_heads, float scale, void* out,
+                                    float* lse, hipStream_t s);
 
 // Last pool row a kernel may touch (pool_rows is clamped to 2^32).
 inline uint32_t pool_last_of(uint64_t pool_rows) {

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <string>
+
 #include "irm_attn.h"
 #include "irm_launch.h"
 
@@ -35,6 +37,9 @@ struct PrefillArgs {
   InvFreq f;
 };
 
+// kFlat: the KV is an assembled cache (row = position, every delta 0), read
+// without row map or rotation; otherwise rows come through the chunk table.
+template <bool kFlat>
 __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) SplitSmem sm;
 
@@ -53,7 +58,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
     load_q<false>(a.q_lat, a.q_rope, min(qi, q_last), a.n_heads, head, qb);
     float m = -INFINITY, l = 0.f;
     __syncthreads();
-    score_stream(a.ra, sm, rows, a.scale_log2,
+    score_stream<kFlat>(a.ra, sm, kFlat ? 0u : a.seq_base[0], rows, a.scale_log2,
                  [&](uint32_t t, uint32_t) -> int32_t {
                    const int64_t last = lim - (int64_t)t * kTileRows;
                    return last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last);
@@ -73,7 +78,8 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  value_stream(a.ra, sm, a.seq_base[0], rows, o, 0, [](uint32_t, const f32x4_t(&)[kSplitGroups][kSplitNb]) {});
+  value_stream<kFlat>(a.ra, sm, kFlat ? 0u : a.seq_base[0], rows, o, 0,
+                      [](uint32_t, const f32x4_t(&)[kSplitGroups][kSplitNb]) {});
   split_publish_wait();
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g) {
@@ -93,14 +99,13 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
 
 }  // namespace
 
-irm_status launch_prefill(const irm_table* t, const void* q_lat, const void* q_rope, int32_t q_pos0,
-                          uint32_t n_q, const void* pool, uint64_t pool_rows, uint32_t n_heads, float scale,
-                          void* out, float* lse, hipStream_t s) {
-  PrefillArgs a;
+namespace {
+
+PrefillArgs prefill_args(const void* q_lat, const void* q_rope, int32_t q_pos0, uint32_t n_q, const void* pool,
+                         uint64_t pool_rows, uint32_t n_heads, float scale, void* out, float* lse) {
+  PrefillArgs a{};
   a.ra.pool = static_cast<const unsigned char*>(pool);
-  a.ra.rowmap = image_of(t).rowmap;
   a.ra.pool_last = pool_last_of(pool_rows);
-  a.seq_base = image_of(t).seq_base;
   a.q_lat = static_cast<const uint4*>(q_lat);
   a.q_rope = static_cast<const uint4*>(q_rope);
   a.out = static_cast<uint16_t*>(out);
@@ -110,11 +115,34 @@ irm_status launch_prefill(const irm_table* t, const void* q_lat, const void* q_r
   a.n_groups = n_heads / 16;
   a.q_pos0 = q_pos0;
   a.scale_log2 = scale * kLog2e;
+  return a;
+}
+
+template <bool kFlat>
+irm_status launch(const PrefillArgs& a, hipStream_t s, const char* fn) {
+  const uint64_t grid = (uint64_t)(a.n_q + kQueriesPerBlock - 1) / kQueriesPerBlock * a.n_groups;
+  if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, std::string(fn) + ": grid too large");
+  hipLaunchKernelGGL(prefill_kernel<kFlat>, dim3((uint32_t)grid), dim3(kRoleThreads), 0, s, a);
+  return launch_check(fn);
+}
+
+}  // namespace
+
+irm_status launch_prefill(const irm_table* t, const void* q_lat, const void* q_rope, int32_t q_pos0,
+                          uint32_t n_q, const void* pool, uint64_t pool_rows, uint32_t n_heads, float scale,
+                          void* out, float* lse, hipStream_t s) {
+  PrefillArgs a = prefill_args(q_lat, q_rope, q_pos0, n_q, pool, pool_rows, n_heads, scale, out, lse);
+  a.ra.rowmap = image_of(t).rowmap;
+  a.seq_base = image_of(t).seq_base;
   for (int i = 0; i < (int)kPairs; ++i) a.f.w[i] = t->inv_freq[i];
-  const uint64_t grid = (uint64_t)(n_q + kQueriesPerBlock - 1) / kQueriesPerBlock * a.n_groups;
-  if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_prefill_tail: grid too large");
-  hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kRoleThreads), 0, s, a);
-  return launch_check("irm_mla_prefill_tail");
+  return launch<false>(a, s, "irm_mla_prefill_tail");
+}
+
+irm_status launch_prefill_assembled(const void* q_lat, const void* q_rope, int32_t q_pos0, uint32_t n_q,
+                                    const void* kv, uint64_t kv_rows, uint32_t n_heads, float scale, void* out,
+                                    float* lse, hipStream_t s) {
+  const PrefillArgs a = prefill_args(q_lat, q_rope, q_pos0, n_q, kv, kv_rows, n_heads, scale, out, lse);
+  return launch<true>(a, s, "irm_mla_prefill_assembled");
 }
 
 }  // namespace irm

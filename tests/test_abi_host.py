@@ -124,3 +124,23 @@ def test_seq_base_is_prefix_sum():
     t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0])
     assert t.seq_base().tolist() == [0, 100, 101, 358, 422]
     assert t.device_bytes % 256 == 0 and t.device_bytes >= 32 * t.n_chunks + 256 * t.n_chunks
+
+
+def test_prefill_assembled_validation_errors():
+    """Argument checks of irm_mla_prefill_assembled come before any HIP call."""
+    import ctypes
+    L = irm.lib()
+    A = 4096  # an aligned stand-in address; validation fails before any use
+    f = L.irm_mla_prefill_assembled
+    def st(q_pos0=0, n_q=1, kv=A, kv_rows=64, heads=16, scale=0.1, q=A, out=A):
+        return irm.STATUS[f(q, q, q_pos0, n_q, kv, kv_rows, heads, ctypes.c_float(scale), out, None, None)]
+    assert st(heads=24) == "EUNSUPPORTED"
+    assert st(heads=256) == "EUNSUPPORTED"
+    assert st(scale=0.0) == "EINVAL"
+    assert st(q_pos0=-1) == "ERANGE"
+    assert st(n_q=0) == "ERANGE"
+    assert st(q_pos0=60, n_q=5) == "ERANGE"
+    assert st(kv=None) == "EINVAL"
+    assert st(kv=A + 8) == "EINVAL"
+    assert st(out=A + 2) == "EINVAL"
+

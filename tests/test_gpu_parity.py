@@ -369,6 +369,46 @@ def test_prefill_short_chunks_and_rescale():
     assert np.max(np.abs(l - l_ref)) <= 4.0 * LSE_TOL  # queries times 4, as in the decode case
 
 
+@pytest.mark.parametrize("seed,heads,N,nq", [(41, 16, 700, 130), (42, 64, 95, 33), (43, 128, 520, 9)])
+def test_prefill_assembled_equals_fused(seed, heads, N, nq):
+    """Assemble with rotate-gather, then prefill over the assembled cache: the
+    same values as the fused path (both round the rotated k_r to bf16 once and
+    run the same MFMA sequence), and within tolerance of the oracle."""
+    w = random_table(seed, [N], heads=heads, p_hit=0.7, prefix_frac=0.25, n_q=nq, kind="prefill")
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    fused = irm.mla_prefill_tail(ql, qr, w.q_pos0, t, pool, scale=w.scale, want_lse=True)
+    kv = irm.rotate_gather(t, pool)
+    asm = irm.mla_prefill_assembled(ql, qr, w.q_pos0, kv, scale=w.scale, want_lse=True)
+    _sync()
+    assert np.array_equal(irm.from_device_bf16(asm[0]), irm.from_device_bf16(fused[0]))
+    assert np.array_equal(asm[1].cpu().numpy(), fused[1].cpu().numpy())
+    o_ref, l_ref = _oracle_prefill(w, None)
+    o = oracle.bf16_to_f64(irm.from_device_bf16(asm[0]))
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(asm[1].cpu().numpy().astype(np.float64) - l_ref)) <= LSE_TOL
+
+
+def test_prefill_assembled_full_size_sampled():
+    """The benchmarked pair: rotate-gather of the 65536-row cache, then 4096
+    queries over it."""
+    w = tail_prefill()
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    kv = irm.rotate_gather(t, pool)
+    out, lse = irm.mla_prefill_assembled(ql, qr, w.q_pos0, kv, scale=w.scale, want_lse=True)
+    _sync()
+    o = oracle.bf16_to_f64(irm.from_device_bf16(out))
+    l = lse.cpu().numpy().astype(np.float64)
+    qids = [0, 1, 2046, 4094, 4095]
+    o_ref, l_ref = _oracle_prefill(w, qids)
+    assert rel_l2(o[qids], o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
+    assert np.all(np.isfinite(o))
+
+
 def test_prefill_last_query_equals_decode():
     w = random_table(26, [1200], heads=16, n_q=7, kind="prefill")
     o, l = _gpu_prefill(w)
