@@ -263,12 +263,14 @@ irm_status irm_mla_prefill_assembled(const void* q_latent, const void* q_rope, i
  */
 typedef struct irm_cdc_params {
   uint64_t seed;
-  uint32_t mask_bits; /* 1..63 */
-  uint32_t min_len;   /* >= 1 */
-  uint32_t max_len;   /* >= min_len */
+  uint32_t mask_bits;       /* 1..63 */
+  uint32_t min_len;         /* >= 1 */
+  uint32_t max_len;         /* >= min_len */
+  uint32_t fallback_window; /* 0: off; else the S1 fallback of irm_registry_assemble with windows of this many tokens */
 } irm_cdc_params;
 
-/* The values the pages fix: mask_bits 7, [min_len, max_len] = [32, 512]; seed 0. */
+/* The values the pages fix: mask_bits 7, [min_len, max_len] = [32, 512]; seed 0;
+ * S1 fallback off (the pages use 128-token windows when it is on). */
 irm_status irm_cdc_params_default(irm_cdc_params* p);
 
 /*
@@ -310,15 +312,23 @@ irm_status irm_registry_info(const irm_registry* r, uint64_t* n_entries, uint64_
  *   registered; fingerprint hit with the same length -> registry entry
  *   (pool_row, len, p_src) placed at pos; otherwise fresh entry on newly
  *   allocated rows, registered with p_src = pos (a stored entry of another
- *   length is replaced).  Fingerprint = xxHash64, seed 0, of the chunk's ids
+ *   length is replaced).  With p->fallback_window = W > 0 (the pages' S1
+ *   fallback: gist.science section 2.2, gentlecold.top section 6), a missed
+ *   chunk is re-split into W-token windows from its start and each is looked
+ *   up: if none hits, the chunk is prefilled on consecutive rows and
+ *   registered together with its windows; otherwise each window becomes its
+ *   own entry (hit, or fresh rows registered as that window).  Fingerprint =
+ *   xxHash64, seed 0, of the chunk's ids
  *   as 4-byte little-endian integers.  Requests are processed in order, so a
  *   chunk inserted by request q is a hit for request q+1.
  *   CDC and fingerprints run on n_threads host threads (0 = all cores).
  *   host out chunks[max_chunks], fingerprints[max_chunks] (optional; 0 for
  *   prefix entries), seq_first[n_req + 1]; *n_chunks = entries.  Every fresh
  *   entry's rows are the caller's to prefill at p_tgt.
- *   ERANGE with *n_chunks = the needed count, and the registry unchanged, if
- *   max_chunks is too small or the allocation counter would pass 2^32 rows.
+ *   ERANGE with *n_chunks = the needed count (with the fallback on, an upper
+ *   bound: every missed chunk counted as all its windows), and the registry
+ *   unchanged, if max_chunks is too small or the allocation counter would
+ *   pass 2^32 rows.
  */
 irm_status irm_registry_assemble(irm_registry* r, const irm_cdc_params* p, const int32_t* tokens,
                                  const uint64_t* tok_first, uint32_t n_req, const uint32_t* prefix_len,

@@ -45,7 +45,7 @@ EXPORTS = (
 class CdcParams(ctypes.Structure):
     """irm_cdc_params: Gear seed, mask bits, chunk length bounds."""
     _fields_ = [("seed", ctypes.c_uint64), ("mask_bits", ctypes.c_uint32), ("min_len", ctypes.c_uint32),
-                ("max_len", ctypes.c_uint32)]
+                ("max_len", ctypes.c_uint32), ("fallback_window", ctypes.c_uint32)]
 
 
 class IrmError(RuntimeError):
@@ -316,8 +316,9 @@ def from_device_bf16(t) -> np.ndarray:
 
 # ---------------------------------------------------------------- chunk-table producer (host)
 def cdc_params(seed: int = 0, mask_bits: Optional[int] = None, min_len: Optional[int] = None,
-               max_len: Optional[int] = None) -> CdcParams:
-    """CDC parameters: the library defaults (mask 7 bits, [32, 512]) unless given."""
+               max_len: Optional[int] = None, fallback_window: int = 0) -> CdcParams:
+    """CDC parameters: the library defaults (mask 7 bits, [32, 512], no S1
+    fallback) unless given; fallback_window=128 is the pages' S1 fallback."""
     p = CdcParams()
     _check(lib().irm_cdc_params_default(ctypes.byref(p)), "irm_cdc_params_default")
     p.seed = int(seed) & (2**64 - 1)
@@ -327,6 +328,7 @@ def cdc_params(seed: int = 0, mask_bits: Optional[int] = None, min_len: Optional
         p.min_len = min_len
     if max_len is not None:
         p.max_len = max_len
+    p.fallback_window = int(fallback_window)
     return p
 
 

@@ -148,6 +148,7 @@ extern "C" irm_status irm_cdc_params_default(irm_cdc_params* p) {
   p->mask_bits = 7;
   p->min_len = 32;
   p->max_len = 512;
+  p->fallback_window = 0;
   return IRM_OK;
 }
 
@@ -254,11 +255,17 @@ extern "C" irm_status irm_registry_assemble(irm_registry* r, const irm_cdc_param
     return fail(IRM_EINVAL, std::string(fn) + ": out of host memory or threads");
   }
 
-  // 2. capacity check before the registry changes
+  // 2. capacity check before the registry changes (with the fallback on, a
+  // missed chunk may become one entry per window: counted as such)
+  const uint32_t W = p->fallback_window;
   uint64_t total = 0;
   for (uint32_t q = 0; q < n_req; ++q) {
     const uint32_t pl = prefix_len ? prefix_len[q] : 0;
-    total += (pl ? (pl > (uint32_t)IRM_CARVE_OUT ? 2 : 1) : 0) + lens[q].size();
+    total += (pl ? (pl > (uint32_t)IRM_CARVE_OUT ? 2 : 1) : 0);
+    if (W == 0)
+      total += lens[q].size();
+    else
+      for (uint32_t n : lens[q]) total += (n + W - 1) / W;
   }
   *n_chunks = (uint32_t)std::min<uint64_t>(total, 0xffffffffull);
   if (total > max_chunks) return fail(IRM_ERANGE, std::string(fn) + ": more entries than max_chunks");
@@ -272,6 +279,13 @@ extern "C" irm_status irm_registry_assemble(irm_registry* r, const irm_cdc_param
   // 3. registry lookups and inserts, in request order
   try {
     uint32_t k = 0;
+    std::vector<uint64_t> wfp;
+    std::vector<char> whit;
+    std::vector<irm_registry::Entry> went;
+    auto lookup = [&](uint64_t f, uint32_t len) -> const irm_registry::Entry* {
+      auto it = r->map.find(f);
+      return (it != r->map.end() && it->second.len == len) ? &it->second : nullptr;
+    };
     auto put = [&](uint32_t row, uint32_t len, int32_t p_src, int32_t p_tgt, uint32_t flags, uint64_t fp) {
       chunks[k] = irm_chunk{row, len, p_src, p_tgt, flags};
       if (fingerprints) fingerprints[k] = fp;
@@ -293,21 +307,58 @@ extern "C" irm_status irm_registry_assemble(irm_registry* r, const irm_cdc_param
         if (pos < IRM_CARVE_OUT) {
           put((uint32_t)r->next_row, n, pos, pos, IRM_FRESH, fp);
           r->next_row += n;
+        } else if (const irm_registry::Entry* e = lookup(fp, n)) {
+          put(e->pool_row, n, e->p_src, pos, 0, fp);
+        } else if (W == 0) {
+          const uint32_t row = (uint32_t)r->next_row;
+          r->next_row += n;
+          r->map[fp] = irm_registry::Entry{row, n, pos};
+          put(row, n, pos, pos, IRM_FRESH, fp);
         } else {
-          auto it = r->map.find(fp);
-          if (it != r->map.end() && it->second.len == n) {
-            put(it->second.pool_row, n, it->second.p_src, pos, 0, fp);
-          } else {
+          // S1: look the chunk's W-token windows up again
+          const int32_t* seg = tokens + tok_first[q] + pos;
+          const uint32_t n_win = (n + W - 1) / W;
+          wfp.resize(n_win);
+          whit.resize(n_win);
+          went.resize(n_win);
+          bool any = false;
+          for (uint32_t k = 0; k < n_win; ++k) {  // every window looked up before any insert
+            const uint32_t o = k * W, len = std::min(W, n - o);
+            wfp[k] = fingerprint(seg + o, len);
+            const irm_registry::Entry* e = lookup(wfp[k], len);
+            whit[k] = e != nullptr;
+            if (e) went[k] = *e;
+            any = any || whit[k];
+          }
+          if (!any) {
             const uint32_t row = (uint32_t)r->next_row;
             r->next_row += n;
             r->map[fp] = irm_registry::Entry{row, n, pos};
+            for (uint32_t k = 0; k < n_win; ++k) {
+              const uint32_t o = k * W;
+              r->map[wfp[k]] = irm_registry::Entry{row + o, std::min(W, n - o), pos + (int32_t)o};
+            }
             put(row, n, pos, pos, IRM_FRESH, fp);
+          } else {
+            for (uint32_t k = 0; k < n_win; ++k) {
+              const uint32_t o = k * W, len = std::min(W, n - o);
+              const int32_t pw = pos + (int32_t)o;
+              if (whit[k]) {
+                put(went[k].pool_row, len, went[k].p_src, pw, 0, wfp[k]);
+              } else {
+                const uint32_t row = (uint32_t)r->next_row;
+                r->next_row += len;
+                r->map[wfp[k]] = irm_registry::Entry{row, len, pw};
+                put(row, len, pw, pw, IRM_FRESH, wfp[k]);
+              }
+            }
           }
         }
         pos += (int32_t)n;
       }
     }
     seq_first[n_req] = k;
+    *n_chunks = k;
   } catch (const std::bad_alloc&) {
     return fail(IRM_EINVAL, std::string(fn) + ": out of host memory (the registry keeps the inserts made so far)");
   }

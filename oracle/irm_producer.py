@@ -40,6 +40,14 @@ Readings where the pages are silent (also listed in the design doc):
   length and first pool row; its first 32 rows are emitted as a fresh entry
   and the rest as an exact-prefix entry (delta 0), as the validator of the
   chunk table wants rows below 32 to be fresh.
+* S1 fallback (gist.science summary, section 2.2; gentlecold.top section 6:
+  a CDC miss is re-split into fixed 128-token windows that are looked up
+  again), when enabled: the windows start at the chunk start (the last one
+  may be shorter); if none hits, the chunk is prefilled on consecutive rows
+  and registered together with each of its windows (pointing into those
+  rows); otherwise every window becomes its own entry, a hit from the
+  registry or a miss on new rows that is registered as a window (the chunk
+  itself, no longer on consecutive rows, is not registered).
 """
 from __future__ import annotations
 
@@ -186,12 +194,18 @@ class Registry:
         self.next_row += n
         return r
 
+    def _lookup(self, fp: int, n: int):
+        hit = self.map.get(fp)
+        return hit if hit is not None and hit[1] == n else None
+
     def assemble(self, tokens, prefix_len: int = 0, prefix_row: int = 0, seed: int = 0,
-                 mask_bits: int = CDC_MASK_BITS, min_len: int = CDC_MIN, max_len: int = CDC_MAX
+                 mask_bits: int = CDC_MASK_BITS, min_len: int = CDC_MIN, max_len: int = CDC_MAX,
+                 fallback_window: int = 0
                  ) -> Tuple[List[Tuple[int, int, int, int, int]], List[Optional[int]]]:
         """Chunk-table entries (pool_row, len, p_src, p_tgt, flags) of one
-        request and the fingerprint of each tail segment (None for prefix
-        entries)."""
+        request and the fingerprint of each entry's tokens (None for prefix
+        entries).  fallback_window > 0 turns on the S1 fallback with windows
+        of that many tokens."""
         entries: List[Tuple[int, int, int, int, int]] = []
         prints: List[Optional[int]] = []
         if prefix_len > 0:
@@ -207,17 +221,38 @@ class Registry:
         for n in cdc_split(tail, seed, mask_bits, min_len, max_len):
             seg = tail[off:off + n]
             fp = chunk_fingerprint(seg)
+            hit = None if p < CARVE_OUT else self._lookup(fp, n)
             if p < CARVE_OUT:
                 entries.append((self._alloc(n), n, p, p, FLAG_FRESH))
+                prints.append(fp)
+            elif hit is not None:
+                entries.append((hit[0], n, hit[2], p, 0))
+                prints.append(fp)
+            elif fallback_window <= 0:
+                row = self._alloc(n)
+                self.map[fp] = (row, n, p)
+                entries.append((row, n, p, p, FLAG_FRESH))
+                prints.append(fp)
             else:
-                hit = self.map.get(fp)
-                if hit is not None and hit[1] == n:
-                    entries.append((hit[0], n, hit[2], p, 0))
-                else:
+                wins = [(o, min(fallback_window, n - o)) for o in range(0, n, fallback_window)]
+                wfps = [chunk_fingerprint(seg[o:o + k]) for o, k in wins]
+                whits = [self._lookup(f, k) for f, (o, k) in zip(wfps, wins)]
+                if all(h is None for h in whits):
                     row = self._alloc(n)
                     self.map[fp] = (row, n, p)
+                    for f, (o, k) in zip(wfps, wins):
+                        self.map[f] = (row + o, k, p + o)
                     entries.append((row, n, p, p, FLAG_FRESH))
-            prints.append(fp)
+                    prints.append(fp)
+                else:
+                    for f, h, (o, k) in zip(wfps, whits, wins):
+                        if h is not None:
+                            entries.append((h[0], k, h[2], p + o, 0))
+                        else:
+                            row = self._alloc(k)
+                            self.map[f] = (row, k, p + o)
+                            entries.append((row, k, p + o, p + o, FLAG_FRESH))
+                        prints.append(f)
             p += n
             off += n
         return entries, prints

@@ -42,12 +42,12 @@ def test_xxh64_matches_oracle():
             assert irm.xxh64(d, s) == P.xxh64(d, s), (n, s)
 
 
-def _oracle_batch(reg, reqs, prefix_len=None, prefix_row=None):
+def _oracle_batch(reg, reqs, prefix_len=None, prefix_row=None, window=0):
     entries, prints, seq_first = [], [], [0]
     for q, r in enumerate(reqs):
         pl = 0 if prefix_len is None else int(prefix_len[q])
         pr = 0 if prefix_row is None else int(prefix_row[q])
-        e, f = reg.assemble(list(r), pl, pr)
+        e, f = reg.assemble(list(r), pl, pr, fallback_window=window)
         entries += e
         prints += [0 if x is None else x for x in f]
         seq_first.append(len(entries))
@@ -62,8 +62,9 @@ def _same(lib_out, ref):
     assert list(seq_first) == ref_sf
 
 
-def test_registry_batches_match_oracle():
-    rng = np.random.default_rng(5)
+@pytest.mark.parametrize("window", [0, 128, 50])
+def test_registry_batches_match_oracle(window):
+    rng = np.random.default_rng(5 + window)
     docs = [list(_toks(rng, int(rng.integers(200, 3000)))) for _ in range(12)]
     lib_reg, ref_reg = irm.Registry(1000), P.Registry(1000)
     for batch in range(4):
@@ -79,8 +80,8 @@ def test_registry_batches_match_oracle():
             pls.append(int(rng.choice([0, 0, 10, 31, 32, 33, min(300, len(parts))])) if parts else 0)
             prs.append(int(rng.integers(0, 100)))
         pls = [min(p, len(r)) for p, r in zip(pls, reqs)]
-        got = lib_reg.assemble(reqs, pls, prs, n_threads=1 + batch % 3)
-        ref = _oracle_batch(ref_reg, reqs, pls, prs)
+        got = lib_reg.assemble(reqs, pls, prs, params=irm.cdc_params(fallback_window=window), n_threads=1 + batch % 3)
+        ref = _oracle_batch(ref_reg, reqs, pls, prs, window)
         _same(got, ref)
         assert lib_reg.info() == (len(ref_reg.map), ref_reg.next_row)
         # the table is valid for the path's own validator (library and oracle)
@@ -141,3 +142,25 @@ def test_producer_error_codes():
     with pytest.raises(irm.IrmError) as e:
         irm.Registry().assemble([np.arange(10, dtype=np.int32)], prefix_len=[11])
     assert e.value.code == "EINVAL"
+
+
+def test_s1_fallback_edge_cases_match_oracle():
+    """Edits inside shared documents (chunks miss, some windows hit), windows
+    repeated inside one chunk, and windows longer than the chunk."""
+    rng = np.random.default_rng(12)
+    doc = list(_toks(rng, 5000))
+    rep = list(_toks(rng, 64)) * 12 + list(_toks(rng, 300))
+    edits = []
+    for k in range(6):
+        d = list(doc)
+        for _ in range(k + 1):
+            d[int(rng.integers(100, 5000))] += 1
+        edits.append(np.array(d, np.int32))
+    for window in (128, 64, 1000):
+        lib_reg, ref_reg = irm.Registry(0), P.Registry(0)
+        for reqs in ([np.array(doc, np.int32), np.array(rep, np.int32)], edits, [np.array(rep[7:], np.int32)]):
+            got = lib_reg.assemble(reqs, params=irm.cdc_params(fallback_window=window))
+            _same(got, _oracle_batch(ref_reg, reqs, window=window))
+            assert lib_reg.info() == (len(ref_reg.map), ref_reg.next_row)
+            irm.Table(got[0], got[1], max(lib_reg.info()[1], 1))
+

@@ -159,3 +159,41 @@ def test_registry_length_mismatch_is_a_miss():
     e, f = reg.assemble(toks[:40] + toks[40:80], seed=0, min_len=40, max_len=40)
     assert f[1] == fp and e[1][4] == P.FLAG_FRESH
     assert reg.map[fp][1] == 40
+
+
+def test_s1_fallback_recovers_windows_of_a_missed_chunk():
+    """gist.science 2.2 / gentlecold.top 6: a CDC miss is re-split into fixed
+    128-token windows and looked up again.  One token changed inside a long
+    chunk: that chunk misses, but its windows that do not hold the change hit
+    at their own positions, and the chunks after it hit whole."""
+    rng = np.random.default_rng(7)
+    doc = list(rng.integers(0, 30000, size=6000))
+    lens = P.cdc_split(doc)
+    starts = np.cumsum([0] + lens[:-1])
+    c = next(i for i in range(1, len(lens)) if lens[i] >= 400 and starts[i] >= 32)
+    x = int(starts[c]) + 200                      # inside window 1 of chunk c, far from its end
+    reg = P.Registry()
+    e1, _ = reg.assemble(doc, fallback_window=128)
+    assert all(e[4] == P.FLAG_FRESH for e in e1)
+    doc2 = list(doc)
+    doc2[x] = (doc2[x] + 1) % 30000
+    assert P.cdc_split(doc2) == lens                 # the change moves no boundary here
+    e2, f2 = reg.assemble(doc2, fallback_window=128)
+    by_pos = {e[3]: e for e in e2}
+    s = int(starts[c])
+    for o in range(0, lens[c], 128):
+        e = by_pos[s + o]
+        assert e[1] == min(128, lens[c] - o)
+        if o <= x - s < o + e[1]:
+            assert e[4] == P.FLAG_FRESH                # the changed window is prefilled
+        else:
+            assert e[4] == 0 and e[2] == e[3]          # the others come back at delta 0
+    for i in range(c + 1, len(lens)):
+        e = by_pos[int(starts[i])]
+        assert e[4] == 0 and e[1] == lens[i]
+    _table_ok(e2, reg.next_row)
+    # without the fallback the whole chunk is prefilled again
+    reg0 = P.Registry()
+    reg0.assemble(doc)
+    e3, _ = reg0.assemble(doc2)
+    assert {e[3]: e for e in e3}[s][1] == lens[c] and {e[3]: e for e in e3}[s][4] == P.FLAG_FRESH
