@@ -223,6 +223,29 @@ irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_rope, int32_
                                 void* out, float* lse, void* stream);
 
 /*
+ * GQA/MHA comparison path (the correction earlier position-independent
+ * caching systems need; gist.science summary, section 1; gentlecold.top
+ * article, sections 3-4): in GQA/MHA the position is folded into the full
+ * key, so every reused row has the whole key of each KV head rotated by
+ * delta (O(N d_K) per KV head), against MLA's 64-wide k_r slice.  Same chunk
+ * table and deltas as irm_rotate_gather.
+ *   Row layout: bf16 [K: n_kv_heads x head_dim | V: n_kv_heads x head_dim];
+ *   device pool [pool_rows][2 * n_kv_heads * head_dim] (16-byte aligned);
+ *   device out [total_rows][same width].  K is turned over the whole
+ *   head_dim with the half-split pairing (element i with i + head_dim/2,
+ *   angle delta * inv_freq[i], host inv_freq[head_dim/2], cos/sin in double
+ *   per entry, the 2x2 rotation in float, RNE to bf16); fresh and delta-0
+ *   rows and all of V are copied bit for bit.
+ *   device ws[irm_gqa_workspace bytes] (16-byte aligned) holds the per-entry
+ *   (cos, sin) table.  head_dim a multiple of 16 in [16, 256], n_kv_heads in
+ *   [1, 256] (EUNSUPPORTED).
+ */
+irm_status irm_gqa_workspace(const irm_table* t, uint32_t head_dim, size_t* bytes);
+irm_status irm_gqa_rotate_gather(const irm_table* t, const void* pool, uint64_t pool_rows, uint32_t n_kv_heads,
+                                 uint32_t head_dim, const double* inv_freq, void* ws, size_t ws_bytes, void* out,
+                                 void* stream);
+
+/*
  * Chunked tail-prefill over an assembled cache (the output of
  * irm_rotate_gather for one sequence): the same causal absorbed MLA attention
  * as irm_mla_prefill_tail, with row r of kv at position r and no rotation

@@ -36,7 +36,8 @@ EXPORTS = (
     "irm_table_info", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
     "irm_table_set_rope",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
-    "irm_mla_decode", "irm_mla_prefill_tail", "irm_mla_prefill_assembled",
+    "irm_mla_decode", "irm_mla_prefill_tail", "irm_mla_prefill_assembled", "irm_gqa_workspace",
+    "irm_gqa_rotate_gather",
     "irm_cdc_params_default", "irm_cdc_split", "irm_xxh64", "irm_registry_create",
     "irm_registry_destroy", "irm_registry_info", "irm_registry_assemble",
 )
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         "irm_mla_decode": (ctypes.c_int, [vp, vp, vp, vp, u64, u32, u32, ctypes.c_float, vp, vp, vp, sz, vp]),
         "irm_mla_prefill_tail": (ctypes.c_int, [vp, vp, i32, u32, vp, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
         "irm_mla_prefill_assembled": (ctypes.c_int, [vp, vp, i32, u32, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
+        "irm_gqa_workspace": (ctypes.c_int, [vp, u32, P(sz)]),
+        "irm_gqa_rotate_gather": (ctypes.c_int, [vp, vp, u64, u32, u32, vp, vp, sz, vp, vp]),
         "irm_cdc_params_default": (ctypes.c_int, [P(CdcParams)]),
         "irm_cdc_split": (ctypes.c_int, [P(CdcParams), vp, u64, vp, u64, P(u64)]),
         "irm_xxh64": (ctypes.c_int, [vp, u64, u64, P(u64)]),
@@ -300,6 +303,32 @@ def mla_prefill_assembled(q_lat, q_rope, q_pos0: int, kv, scale: float = DEFAULT
                                            float(scale), _ptr(out), _ptr(lse), _stream(stream)),
            "irm_mla_prefill_assembled")
     return (out, lse) if want_lse else out
+
+
+def gqa_inv_freq(theta: float, head_dim: int) -> np.ndarray:
+    """theta^(-2i/head_dim), i < head_dim/2 (plain RoPE frequencies of a GQA head)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return theta ** (-2.0 * i / head_dim)
+
+
+def gqa_rotate_gather(table: Table, pool, n_kv_heads: int, head_dim: int, inv_freq, out=None, stream=None):
+    """Assemble GQA rows (bf16 [K heads | V heads]) with the whole key of each
+    KV head rotated by the entry's delta (the GQA/MHA comparison path)."""
+    import torch
+    width = 2 * n_kv_heads * head_dim
+    _bf16_2d(pool, width, "pool")
+    inv = np.ascontiguousarray(inv_freq, dtype=np.float64)
+    if inv.size != head_dim // 2:
+        raise ValueError("inv_freq must hold head_dim / 2 values")
+    if out is None:
+        out = torch.empty((table.total_rows, width), dtype=torch.bfloat16, device=pool.device)
+    nb = ctypes.c_size_t()
+    _check(lib().irm_gqa_workspace(table.handle, head_dim, ctypes.byref(nb)), "irm_gqa_workspace")
+    ws = torch.empty(max(16, nb.value), dtype=torch.uint8, device=pool.device)
+    _check(lib().irm_gqa_rotate_gather(table.handle, _ptr(pool), pool.shape[0], n_kv_heads, head_dim,
+                                       inv.ctypes.data, _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
+           "irm_gqa_rotate_gather")
+    return out
 
 
 def to_device_bf16(bits: np.ndarray):

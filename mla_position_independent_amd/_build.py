@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libirm.so")
 
-SOURCES = ["irm_table.cpp", "irm_abi.cpp", "irm_producer.cpp", "irm_gather.hip", "irm_decode.hip", "irm_prefill.hip"]
+SOURCES = ["irm_table.cpp", "irm_abi.cpp", "irm_producer.cpp", "irm_gather.hip", "irm_decode.hip", "irm_prefill.hip",
+           "irm_gqa.hip"]
 DEPS = SOURCES + ["irm_internal.h", "irm_device.h", "irm_attn.h", "irm_launch.h"]
 
 

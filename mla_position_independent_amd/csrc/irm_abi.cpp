@@ -204,3 +204,46 @@ extern "C" irm_status irm_mla_prefill_assembled(const void* q_latent, const void
   return irm::launch_prefill_assembled(q_latent, q_rope, q_pos0, n_q, kv, kv_rows, n_heads, scale, out, lse,
                                        static_cast<hipStream_t>(stream));
 }
+
+// ---------------------------------------------------------------------------
+// GQA/MHA comparison path
+// ---------------------------------------------------------------------------
+namespace {
+irm_status check_gqa_shape(uint32_t n_kv_heads, uint32_t head_dim, const char* fn) {
+  if (head_dim < 16 || head_dim > irm::kGqaMaxHeadDim || head_dim % 16)
+    return fail(IRM_EUNSUPPORTED, std::string(fn) + ": head_dim must be a multiple of 16 in [16, 256]");
+  if (n_kv_heads < 1 || n_kv_heads > 256)
+    return fail(IRM_EUNSUPPORTED, std::string(fn) + ": n_kv_heads must be in [1, 256]");
+  return IRM_OK;
+}
+}  // namespace
+
+extern "C" irm_status irm_gqa_workspace(const irm_table* t, uint32_t head_dim, size_t* bytes) {
+  if (!t || !bytes) return fail(IRM_EINVAL, "irm_gqa_workspace: NULL argument");
+  irm_status st = check_gqa_shape(1, head_dim, "irm_gqa_workspace");
+  if (st != IRM_OK) return st;
+  *bytes = (size_t)t->n_chunks * (head_dim / 2) * 8;
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_gqa_rotate_gather(const irm_table* t, const void* pool, uint64_t pool_rows,
+                                            uint32_t n_kv_heads, uint32_t head_dim, const double* inv_freq,
+                                            void* ws, size_t ws_bytes, void* out, void* stream) {
+  static const char* fn = "irm_gqa_rotate_gather";
+  irm_status st = need_uploaded(t, fn);
+  if (st != IRM_OK) return st;
+  if ((st = check_gqa_shape(n_kv_heads, head_dim, fn)) != IRM_OK) return st;
+  if (!inv_freq) return fail(IRM_EINVAL, std::string(fn) + ": inv_freq is NULL");
+  for (uint32_t i = 0; i < head_dim / 2; ++i)
+    if (!std::isfinite(inv_freq[i])) return fail(IRM_EINVAL, std::string(fn) + ": inv_freq must be finite");
+  if ((st = check_pool(t, pool, pool_rows, fn)) != IRM_OK) return st;
+  const size_t need = (size_t)t->n_chunks * (head_dim / 2) * 8;
+  if (need && (!ws || ws_bytes < need || !aligned16(ws)))
+    return fail(IRM_EWORKSPACE, std::string(fn) + ": workspace missing, unaligned or smaller than irm_gqa_workspace");
+  if (t->total_rows && (!out || !aligned16(out)))
+    return fail(IRM_EINVAL, std::string(fn) + ": out must be non-NULL and 16-byte aligned");
+  if ((st = check_device()) != IRM_OK) return st;
+  return irm::launch_gqa_rotate_gather(t, pool, n_kv_heads, head_dim, inv_freq, static_cast<float2*>(ws), out,
+                                       static_cast<hipStream_t>(stream));
+}
+

@@ -30,6 +30,9 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
 irm_status launch_prefill(const irm_table* t, const void* q_lat, const void* q_rope, int32_t q_pos0,
                           uint32_t n_q, const void* pool, uint64_t pool_rows, uint32_t n_heads, float scale,
                           void* out, float* lse, hipStream_t s);
+constexpr uint32_t kGqaMaxHeadDim = 256;
+irm_status launch_gqa_rotate_gather(const irm_table* t, const void* pool, uint32_t n_kv_heads, uint32_t head_dim,
+                                    const double* inv_freq, float2* trig, void* out, hipStream_t s);
 irm_status launch_prefill_assembled(const void* q_lat, const void* q_rope, int32_t q_pos0, uint32_t n_q,
                                     const void* kv, uint64_t kv_rows, uint32_t n_heads, float scale, void* out,
                                     float* lse, hipStream_t s);

@@ -170,6 +170,75 @@ def test_rotate_gather_full_size_sampled():
     assert w_rows.shape[0] == rows.shape[0]
 
 
+# ---------------------------------------------------------------- GQA/MHA comparison path
+def _check_gqa(w, pool_bits, out_bits, H, d, rows=None):
+    from oracle import irm_gqa
+    inv = irm_gqa.gqa_inv_freq(1e6, d)
+    k_ref, v_ref, gather, delta = irm_gqa.gqa_rotate_gather(pool_bits, w.chunks, w.seq_first, H, d, inv)
+    if rows is not None:
+        k_ref, v_ref, gather, delta = k_ref[rows], v_ref[rows], gather[rows], delta[rows]
+    kd = H * d
+    assert np.array_equal(out_bits[:, kd:], v_ref)                      # V bit for bit
+    same = delta == 0
+    assert np.array_equal(out_bits[same, :kd], pool_bits[gather[same], :kd])   # unrotated K bit for bit
+    got = oracle.bf16_to_f64(out_bits[:, :kd]).reshape(-1, H, d)
+    src = oracle.bf16_to_f64(pool_bits[gather, :kd]).reshape(-1, H, d)
+    assert np.all(np.abs(got - k_ref) <= _rot_bound(k_ref, src)), np.max(np.abs(got - k_ref) / _rot_bound(k_ref, src))
+    return int(np.sum(~same))
+
+
+def _rot_bound(exact, src):
+    """Error bound of a pair rotation computed in float and rounded to bf16:
+    one bf16 ulp of the exact value (the rounding, with slack) plus 2^-21 of
+    |x| + |y| (products, float cos/sin and the sum, which matter where the
+    result cancels to near zero)."""
+    h = src.shape[-1] // 2
+    pair = np.abs(src[..., :h]) + np.abs(src[..., h:])
+    return _bf16_ulp(exact) * 1.0000001 + 2.0 ** -21 * np.concatenate([pair, pair], axis=-1)
+
+
+@pytest.mark.parametrize("seed,H,d", [(51, 8, 128), (52, 1, 64), (53, 4, 16), (54, 2, 256), (55, 3, 48)])
+def test_gqa_rotate_gather(seed, H, d):
+    from oracle import irm_gqa
+    w = random_table(seed, [700, 33, 1500, 5], p_hit=0.7, prefix_frac=0.2)
+    rng = np.random.default_rng(seed)
+    from synth import randn_bf16
+    pool_bits = randn_bf16(rng, (w.pool.shape[0], 2 * H * d))
+    t = _table(w)
+    out = irm.gqa_rotate_gather(t, irm.to_device_bf16(pool_bits), H, d, irm_gqa.gqa_inv_freq(1e6, d))
+    _sync()
+    assert _check_gqa(w, pool_bits, irm.from_device_bf16(out), H, d) > 100
+
+
+def test_gqa_rotate_gather_full_size_sampled():
+    """The rotate-gather batch (64 x 32768 tokens) over a GQA pool of 8 KV
+    heads x 128 (4 KB rows), drawn on the device; sampled rows checked."""
+    import torch
+    from oracle import irm_gqa
+    w = rotate_gather_batch()
+    H, d = 8, 128
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    pool = torch.randn((w.pool.shape[0], 2 * H * d), generator=g, device="cuda").to(torch.bfloat16)
+    t = _table(w)
+    out = irm.gqa_rotate_gather(t, pool, H, d, irm_gqa.gqa_inv_freq(1e6, d))
+    _sync()
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(t.total_rows, size=3000, replace=False))
+    idx = torch.from_numpy(rows).cuda()
+    out_s = irm.from_device_bf16(out.index_select(0, idx))
+    exp = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
+    gather = np.concatenate([x for x, _, _ in exp])
+    pool_s = irm.from_device_bf16(pool.index_select(0, torch.from_numpy(gather[rows]).cuda()))
+    delta = np.concatenate([x for _, x, _ in exp])[rows]
+    k_ref = irm_gqa.rotate_half_split(oracle.bf16_to_f64(pool_s[:, :H * d]).reshape(-1, H, d), delta[:, None],
+                                      irm_gqa.gqa_inv_freq(1e6, d))
+    assert np.array_equal(out_s[:, H * d:], pool_s[:, H * d:])
+    got = oracle.bf16_to_f64(out_s[:, :H * d]).reshape(-1, H, d)
+    src = oracle.bf16_to_f64(pool_s[:, :H * d]).reshape(-1, H, d)
+    assert np.all(np.abs(got - k_ref) <= _rot_bound(k_ref, src))
+    assert np.array_equal(out_s[delta == 0, :H * d], pool_s[delta == 0, :H * d])
+
+
 # ---------------------------------------------------------------- decode
 def _oracle_decode(w, seqs, heads=None):
     inv = oracle.rope_inv_freq(w.theta)
