@@ -8,10 +8,11 @@ the rotate-gather kernel, with the chunk table's device image and the pool
 already resident in HBM.  ``value`` is assembled KV tokens per second.
 
 Further legs time MLA decode with rotation on load (batch 64 x 8192 tokens
-x 16 heads; batch 32 x 32768 x 128 heads with 16 splits) and the chunked
+x 16 heads; batch 32 x 32768 x 128 heads with 16 splits), the chunked
 tail-prefill (4096 queries over 65536 rows, 16 heads: rotate-gather of the
-cache, then the prefill over it) with the same methodology, each with its own
-roofline, and the host chunk-table producer
+cache, then the prefill over it) and the GQA/MHA comparison (the same chunk
+table over an 8 x 128 grouped-query pool with the whole key rotated) with the
+same methodology, each with its own roofline, and the host chunk-table producer
 (content-defined chunking, fingerprints and registry lookups for 64 requests
 x 32768 tokens against a warm registry; host work, no GPU).  The CPU oracle
 is timed on a bounded sample of the rotate-gather batch as ``cpu_baseline``
@@ -43,6 +44,7 @@ KERNEL_SOURCES = {
     "decode_private_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
     "decode_shared_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
     "prefill_kernel": ["irm_prefill.hip", "irm_attn.h", "irm_device.h"],
+    "gqa_rotate_gather_kernel": ["irm_gqa.hip", "irm_device.h"],
 }
 
 
@@ -265,6 +267,45 @@ def leg_prefill(args, irm, torch, synth):
     }
 
 
+def leg_gqa(args, irm, torch, gather):
+    """GQA/MHA comparison: the rotate-gather batch's chunk table over a
+    grouped-query pool (8 KV heads x head_dim 128, rows [K | V] = 4096 B),
+    where every reused row has its whole key rotated.  Same methodology as the
+    MLA rotate-gather leg; the pool is drawn on the device (seeded)."""
+    n_kv, d = 8, 128
+    t, w = gather["table"], gather["workload"]
+    width = 2 * n_kv * d
+    log(f"gqa rotate-gather: drawing a {w.pool.shape[0]} x {width} bf16 pool on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3003)
+    pool = torch.randn((w.pool.shape[0], width), dtype=torch.bfloat16, device="cuda", generator=gen)
+    out = torch.empty((t.total_rows, width), dtype=torch.bfloat16, device="cuda")
+    inv = irm.gqa_inv_freq(w.theta, d)
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        irm.gqa_rotate_gather(t, pool, n_kv, d, inv, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    tokens = t.total_rows
+    alg_bytes = 2 * 2 * width * tokens
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    ratio = kern_ms / gather["kernel_ms"]
+    log(f"gqa rotate-gather: {kern_ms:.3f} ms/call, {achieved:.0f} GB/s; {ratio:.2f}x the MLA rotate-gather time")
+    return {
+        "workload": f"gqa_{n_kv}x{d}_" + w.name, "ms_per_call": round(kern_ms, 4), "tokens": tokens,
+        "row_bytes": 2 * width, "rotated_bytes_per_token": n_kv * d * 2, "mla_rotated_bytes_per_token": 128,
+        "time_vs_mla_rotate_gather": round(ratio, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gqa_rotate_gather_kernel"),
+                     "kernel": "gqa_trig_kernel + gqa_rotate_gather_kernel",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+    }
+
+
 def leg_producer(args, irm, synth, oracle_seconds: float):
     """Host chunk-table producer: irm_registry_assemble on 64 requests x 32768
     tokens (shared documents at shifted offsets, 80% of segments), the
@@ -354,7 +395,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="gather,decode,long_decode,prefill,producer",
+    ap.add_argument("--legs", default="gather,decode,long_decode,prefill,gqa,producer",
                     help="comma list; without gather only the named legs run (profiling, no JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -397,9 +438,10 @@ def main():
     legs = [x.strip() for x in args.legs.split(",") if x.strip()]
     if args.profile or "gather" not in legs:
         # profiling mode: run the requested legs only, no JSON line
+        g = None
         for name in legs:
             if name == "gather":
-                leg_gather(args, irm, torch, synth)
+                g = leg_gather(args, irm, torch, synth)
             elif name == "decode":
                 leg_decode(args, irm, torch, synth, "batched decode", synth.batched_decode)
             elif name == "long_decode":
@@ -408,6 +450,8 @@ def main():
                 leg_prefill(args, irm, torch, synth)
             elif name == "producer":
                 leg_producer(args, irm, synth, 0.0)
+            elif name == "gqa":
+                leg_gqa(args, irm, torch, leg_gather(args, irm, torch, synth) if g is None else g)
         return
     g = leg_gather(args, irm, torch, synth)
     extra = {}
@@ -417,6 +461,8 @@ def main():
         extra["long_decode"] = leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)
     if "prefill" in legs:
         extra["prefill"] = leg_prefill(args, irm, torch, synth)
+    if "gqa" in legs:
+        extra["gqa_comparison"] = leg_gqa(args, irm, torch, g)
     if "producer" in legs:
         extra["producer"] = leg_producer(args, irm, synth, 0.0 if args.no_cpu_baseline else 3.0)
 

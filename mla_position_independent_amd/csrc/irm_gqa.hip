@@ -50,6 +50,7 @@ struct GqaShape {
   uint32_t row_units;   // units per row (n_kv_heads * head_dim / 4)
   uint32_t items;       // items per row (n_pairs + n_kv_heads * head_dim / 8)
   uint32_t half;        // rotation pairs per head (head_dim / 2)
+  uint64_t recip;       // ceil(2^64 / items): item / items == umulhi(item, recip) for item < 2^64 / items
 };
 
 __device__ __forceinline__ u32x4_t turn(const u32x4_t& a, const u32x4_t& b, const float2* cs, bool hi) {
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_gather_kernel(const uint4
 #pragma unroll
     for (int k = 0; k < kItemsInFlight; ++k) {
       const uint64_t it = min(base + (uint64_t)k * kThreads + threadIdx.x, n_items - 1);
-      row[k] = it / g.items;
+      row[k] = __umul64hi(it, g.recip);
       col[k] = (uint32_t)(it - row[k] * g.items);
       rec[k] = rowmap[row[k]];
     }
@@ -145,6 +146,11 @@ irm_status launch_gqa_rotate_gather(const irm_table* t, const void* pool, uint32
   g.row_units = n_kv_heads * head_dim / 4;
   g.items = g.n_pairs + n_kv_heads * head_dim / 8;
   g.half = half;
+  // exact quotient by multiplication (Granlund and Montgomery, "Division by
+  // invariant integers using multiplication", 1994): with recip = ceil(2^64 / d)
+  // the error term stays below one for numerators under 2^64 / d; items <= 12288
+  // and rows < 2^32 keep every item index far below that
+  g.recip = (uint64_t)((((unsigned __int128)1 << 64) + g.items - 1) / g.items);
   const uint64_t n_items = t->total_rows * g.items;
   const uint64_t steps = (n_items + kGqaStep - 1) / kGqaStep;
   const uint32_t grid = (uint32_t)(steps < 0x7fffffffull ? steps : 0x7fffffffull);
