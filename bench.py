@@ -10,7 +10,8 @@ already resident in HBM.  ``value`` is assembled KV tokens per second.
 Further legs time MLA decode with rotation on load (batch 64 x 8192 tokens
 x 16 heads; batch 32 x 32768 x 128 heads with 16 splits), the chunked
 tail-prefill (4096 queries over 65536 rows, 16 heads: rotate-gather of the
-cache, then the prefill over it) and the GQA/MHA comparison (the same chunk
+cache, then the prefill over it), its non-absorbed form (per-head up-projection
+of the assembled cache, then attention with 192-wide keys) and the GQA/MHA comparison (the same chunk
 table over an 8 x 128 grouped-query pool with the whole key rotated) with the
 same methodology, each with its own roofline, and the host chunk-table producer
 (content-defined chunking, fingerprints and registry lookups for 64 requests
@@ -45,6 +46,7 @@ KERNEL_SOURCES = {
     "decode_shared_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
     "prefill_kernel": ["irm_prefill.hip", "irm_attn.h", "irm_device.h"],
     "gqa_rotate_gather_kernel": ["irm_gqa.hip", "irm_device.h"],
+    "mha_prefill_kernel": ["irm_nonabsorbed.hip", "irm_attn.h", "irm_device.h"],
 }
 
 
@@ -267,6 +269,59 @@ def leg_prefill(args, irm, torch, synth):
     }
 
 
+def leg_nonabsorbed(args, irm, torch, synth):
+    """Non-absorbed MLA prefill on the tail-prefill workload: the assembled
+    65536-row cache is up-projected per head (irm_mla_kv_upproj, random
+    W_UK / W_UV), then the 4096 queries attend with 192-wide keys and 128-wide
+    values per head (irm_mla_prefill_nonabsorbed).  Roofline on the attention
+    kernel; the up-projection is timed on its own."""
+    log("non-absorbed prefill: generating")
+    w = synth.tail_prefill()
+    pool = irm.to_device_bf16(w.pool)
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(irm.rope_inv_freq(w.theta))
+    q_nope, wk, wv = synth.nonabsorbed_inputs(1005, w.q_lat.shape[0], w.n_heads)
+    qn, qr = irm.to_device_bf16(q_nope), irm.to_device_bf16(w.q_rope)
+    wk, wv = irm.to_device_bf16(wk), irm.to_device_bf16(wv)
+    nq, H = qn.shape[0], qn.shape[1]
+    kv = irm.rotate_gather(t, pool)
+    kvh = torch.empty((H, kv.shape[0], 256), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((nq, H, 128), dtype=torch.bfloat16, device="cuda")
+
+    def up(ev):
+        if ev is not None:
+            ev[0].record()
+        irm.mla_kv_upproj(kv, wk, wv, out=kvh)
+        if ev is not None:
+            ev[1].record()
+
+    def attend(ev):
+        if ev is not None:
+            ev[0].record()
+        irm.mla_prefill_nonabsorbed(qn, qr, w.q_pos0, kv, kvh, scale=w.scale, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    n_steps = max(2, args.steps // 2)
+    _, up_ms = time_leg(up, n_steps, min(args.warmup, 2))
+    _, kern_ms = time_leg(attend, n_steps, min(args.warmup, 2))
+    pairs = nq * w.q_pos0 + nq * (nq + 1) // 2
+    flops = pairs * H * 2 * (192 + 128)
+    up_flops = 2 * kv.shape[0] * 512 * 256 * H
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    up_tfs = up_flops / (up_ms * 1e-3) / 1e12
+    log(f"non-absorbed prefill: up-projection {up_ms:.3f} ms ({up_tfs:.0f} TFLOP/s), attention {kern_ms:.3f} ms "
+        f"({achieved:.0f} TFLOP/s)")
+    return {
+        "workload": w.name + "_nonabsorbed", "ms_per_call": round(up_ms + kern_ms, 4), "queries": nq,
+        "kv_rows": int(kv.shape[0]), "call": "irm_mla_kv_upproj + irm_mla_prefill_nonabsorbed (over the assembled cache)",
+        "upproj_ms": round(up_ms, 4), "upproj_tflops": round(up_tfs, 1), "attention_ms": round(kern_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                     "traffic": measured_traffic("mha_prefill_kernel"), "kernel": "mha_prefill_kernel",
+                     "algorithmic_flops_per_launch": flops},
+    }
+
+
 def leg_gqa(args, irm, torch, gather):
     """GQA/MHA comparison: the rotate-gather batch's chunk table over a
     grouped-query pool (8 KV heads x head_dim 128, rows [K | V] = 4096 B),
@@ -395,7 +450,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="gather,decode,long_decode,prefill,gqa,producer",
+    ap.add_argument("--legs", default="gather,decode,long_decode,prefill,nonabsorbed,gqa,producer",
                     help="comma list; without gather only the named legs run (profiling, no JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -450,6 +505,8 @@ def main():
                 leg_prefill(args, irm, torch, synth)
             elif name == "producer":
                 leg_producer(args, irm, synth, 0.0)
+            elif name == "nonabsorbed":
+                leg_nonabsorbed(args, irm, torch, synth)
             elif name == "gqa":
                 leg_gqa(args, irm, torch, leg_gather(args, irm, torch, synth) if g is None else g)
         return
@@ -461,6 +518,8 @@ def main():
         extra["long_decode"] = leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)
     if "prefill" in legs:
         extra["prefill"] = leg_prefill(args, irm, torch, synth)
+    if "nonabsorbed" in legs:
+        extra["prefill_nonabsorbed"] = leg_nonabsorbed(args, irm, torch, synth)
     if "gqa" in legs:
         extra["gqa_comparison"] = leg_gqa(args, irm, torch, g)
     if "producer" in legs:

@@ -261,6 +261,36 @@ irm_status irm_mla_prefill_assembled(const void* q_latent, const void* q_rope, i
                                      uint32_t n_q, const void* kv, uint64_t kv_rows, uint32_t n_heads,
                                      float scale, void* out, float* lse, void* stream);
 
+/*
+ * Non-absorbed MLA prefill, step 1: up-project the latent rows of an
+ * assembled cache to a full key and value per head (gentlecold.top article,
+ * section 4: key [W_UK c_KV, k_r], value from c_KV; section 13: a
+ * non-absorbed model has to up-project c_KV at run time).
+ *   device kv bf16 [kv_rows][576] (c_KV = the first 512; 16-byte aligned);
+ *   device w_uk, w_uv bf16 [n_heads][128][512] (output feature, latent input;
+ *   16-byte aligned); device out bf16 [n_heads][kv_rows][256] = per head and
+ *   row [W_UK[h] c_KV | W_UV[h] c_KV] (16-byte aligned), float accumulation,
+ *   RNE to bf16.  n_heads in [1, 128], kv_rows < 2^32 (EUNSUPPORTED).
+ */
+irm_status irm_mla_kv_upproj(const void* kv, uint64_t kv_rows, const void* w_uk, const void* w_uv,
+                             uint32_t n_heads, void* out, void* stream);
+
+/*
+ * Non-absorbed MLA prefill, step 2: causal attention of every head with its
+ * own key [k_nope (128) | k_r (64)] and value (128), k_r being the rotated
+ * slice of the assembled row shared by all heads; score scale `scale`
+ * (1/sqrt(192) for the 128 + 64 key).
+ *   device q_nope bf16 [n_q][n_heads][128], q_rope bf16 [n_q][n_heads][64]
+ *   (already RoPE'd at its position); kv as in irm_mla_kv_upproj (for k_r);
+ *   kvh = that call's out; device out bf16 [n_q][n_heads][128]; lse float
+ *   [n_q][n_heads] (natural log, optional).  Query i at q_pos0 + i attends
+ *   rows t <= q_pos0 + i.  0 <= q_pos0, 1 <= n_q, q_pos0 + n_q <= kv_rows
+ *   (ERANGE); n_heads in [1, 128], kv_rows < 2^32 (EUNSUPPORTED).
+ */
+irm_status irm_mla_prefill_nonabsorbed(const void* q_nope, const void* q_rope, int32_t q_pos0, uint32_t n_q,
+                                       const void* kv, const void* kvh, uint64_t kv_rows, uint32_t n_heads,
+                                       float scale, void* out, float* lse, void* stream);
+
 /* ------------------------------------------------------------------------
  * Host chunk-table producer (no HIP call; usable without a GPU).
  *

@@ -37,7 +37,7 @@ EXPORTS = (
     "irm_table_set_rope",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
     "irm_mla_decode", "irm_mla_prefill_tail", "irm_mla_prefill_assembled", "irm_gqa_workspace",
-    "irm_gqa_rotate_gather",
+    "irm_gqa_rotate_gather", "irm_mla_kv_upproj", "irm_mla_prefill_nonabsorbed",
     "irm_cdc_params_default", "irm_cdc_split", "irm_xxh64", "irm_registry_create",
     "irm_registry_destroy", "irm_registry_info", "irm_registry_assemble",
 )
@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
         "irm_mla_prefill_tail": (ctypes.c_int, [vp, vp, i32, u32, vp, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
         "irm_mla_prefill_assembled": (ctypes.c_int, [vp, vp, i32, u32, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
         "irm_gqa_workspace": (ctypes.c_int, [vp, u32, P(sz)]),
+        "irm_mla_kv_upproj": (ctypes.c_int, [vp, u64, vp, vp, u32, vp, vp]),
+        "irm_mla_prefill_nonabsorbed": (ctypes.c_int, [vp, vp, i32, u32, vp, vp, u64, u32, ctypes.c_float, vp, vp,
+                                                       vp]),
         "irm_gqa_rotate_gather": (ctypes.c_int, [vp, vp, u64, u32, u32, vp, vp, sz, vp, vp]),
         "irm_cdc_params_default": (ctypes.c_int, [P(CdcParams)]),
         "irm_cdc_split": (ctypes.c_int, [P(CdcParams), vp, u64, vp, u64, P(u64)]),
@@ -302,6 +305,53 @@ def mla_prefill_assembled(q_lat, q_rope, q_pos0: int, kv, scale: float = DEFAULT
     _check(lib().irm_mla_prefill_assembled(_ptr(q_lat), _ptr(q_rope), int(q_pos0), nq, _ptr(kv), kv.shape[0], H,
                                            float(scale), _ptr(out), _ptr(lse), _stream(stream)),
            "irm_mla_prefill_assembled")
+    return (out, lse) if want_lse else out
+
+
+D_NOPE = 128   # per-head nope key width of the non-absorbed form
+D_V = 128      # per-head value width of the non-absorbed form
+
+
+def mla_kv_upproj(kv, w_uk, w_uv, out=None, stream=None):
+    """Per-head up-projection of an assembled cache: kv bf16 [rows][576],
+    w_uk / w_uv bf16 [H][128][512] -> bf16 [H][rows][256] = [W_UK c_KV | W_UV c_KV]."""
+    import torch
+    _bf16_2d(kv, ROW, "kv")
+    _bf16_2d(w_uk, D_LATENT, "w_uk")
+    _bf16_2d(w_uv, D_LATENT, "w_uv")
+    H = w_uk.shape[0]
+    if tuple(w_uk.shape) != (H, D_NOPE, D_LATENT) or tuple(w_uv.shape) != (H, D_V, D_LATENT):
+        raise ValueError("w_uk and w_uv must be [H][128][512]")
+    rows = kv.shape[0]
+    if out is None:
+        out = torch.empty((H, rows, D_NOPE + D_V), dtype=torch.bfloat16, device=kv.device)
+    elif tuple(out.shape) != (H, rows, D_NOPE + D_V):
+        raise ValueError("out must be [H][rows][256]")
+    _check(lib().irm_mla_kv_upproj(_ptr(kv), rows, _ptr(w_uk), _ptr(w_uv), H, _ptr(out), _stream(stream)),
+           "irm_mla_kv_upproj")
+    return out
+
+
+def mla_prefill_nonabsorbed(q_nope, q_rope, q_pos0: int, kv, kvh, scale: float = DEFAULT_SCALE, out=None,
+                            want_lse: bool = False, stream=None):
+    """Causal prefill with per-head keys [k_nope | k_r] and values from
+    mla_kv_upproj (kvh bf16 [H][rows][256]); k_r from the assembled kv."""
+    import torch
+    _bf16_2d(kv, ROW, "kv")
+    _bf16_2d(kvh, D_NOPE + D_V, "kvh")
+    _bf16_2d(q_nope, D_NOPE, "q_nope")
+    _bf16_2d(q_rope, D_ROPE, "q_rope")
+    nq, H = q_nope.shape[0], q_nope.shape[1]
+    if tuple(q_rope.shape) != (nq, H, D_ROPE):
+        raise ValueError("q_rope must be [n_q][H][64]")
+    if tuple(kvh.shape) != (H, kv.shape[0], D_NOPE + D_V):
+        raise ValueError("kvh must be [H][rows][256] for the rows of kv")
+    if out is None:
+        out = torch.empty((nq, H, D_V), dtype=torch.bfloat16, device=kv.device)
+    lse = torch.empty((nq, H), dtype=torch.float32, device=kv.device) if want_lse else None
+    _check(lib().irm_mla_prefill_nonabsorbed(_ptr(q_nope), _ptr(q_rope), int(q_pos0), nq, _ptr(kv), _ptr(kvh),
+                                             kv.shape[0], H, float(scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "irm_mla_prefill_nonabsorbed")
     return (out, lse) if want_lse else out
 
 

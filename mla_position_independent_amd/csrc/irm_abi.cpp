@@ -206,6 +206,48 @@ extern "C" irm_status irm_mla_prefill_assembled(const void* q_latent, const void
 }
 
 // ---------------------------------------------------------------------------
+// Non-absorbed prefill
+// ---------------------------------------------------------------------------
+namespace {
+irm_status check_na_shape(uint64_t kv_rows, uint32_t n_heads, const char* fn) {
+  if (n_heads < 1 || n_heads > 128) return fail(IRM_EUNSUPPORTED, std::string(fn) + ": n_heads must be in [1, 128]");
+  if (kv_rows >= 0x100000000ull) return fail(IRM_EUNSUPPORTED, std::string(fn) + ": fewer than 2^32 cache rows");
+  return IRM_OK;
+}
+}  // namespace
+
+extern "C" irm_status irm_mla_kv_upproj(const void* kv, uint64_t kv_rows, const void* w_uk, const void* w_uv,
+                                        uint32_t n_heads, void* out, void* stream) {
+  static const char* fn = "irm_mla_kv_upproj";
+  irm_status st = check_na_shape(kv_rows, n_heads, fn);
+  if (st != IRM_OK) return st;
+  if (kv_rows && (!kv || !w_uk || !w_uv || !out || !aligned16(kv) || !aligned16(w_uk) || !aligned16(w_uv) ||
+                  !aligned16(out)))
+    return fail(IRM_EINVAL, std::string(fn) + ": kv, w_uk, w_uv and out must be non-NULL and 16-byte aligned");
+  if ((st = check_device()) != IRM_OK) return st;
+  return irm::launch_kv_upproj(kv, kv_rows, w_uk, w_uv, n_heads, out, static_cast<hipStream_t>(stream));
+}
+
+extern "C" irm_status irm_mla_prefill_nonabsorbed(const void* q_nope, const void* q_rope, int32_t q_pos0,
+                                                  uint32_t n_q, const void* kv, const void* kvh, uint64_t kv_rows,
+                                                  uint32_t n_heads, float scale, void* out, float* lse,
+                                                  void* stream) {
+  static const char* fn = "irm_mla_prefill_nonabsorbed";
+  irm_status st = check_na_shape(kv_rows, n_heads, fn);
+  if (st != IRM_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(IRM_EINVAL, std::string(fn) + ": scale must be finite and > 0");
+  if (q_pos0 < 0 || n_q == 0 || (uint64_t)q_pos0 + n_q > kv_rows)
+    return fail(IRM_ERANGE, std::string(fn) + ": queries must satisfy 0 <= q_pos0, 1 <= n_q, q_pos0 + n_q <= kv_rows");
+  if (!kv || !kvh || !aligned16(kv) || !aligned16(kvh))
+    return fail(IRM_EINVAL, std::string(fn) + ": kv and kvh must be non-NULL and 16-byte aligned");
+  if (!q_nope || !q_rope || !out || !aligned16(q_nope) || !aligned16(q_rope) || !aligned16(out))
+    return fail(IRM_EINVAL, std::string(fn) + ": q_nope, q_rope and out must be non-NULL and 16-byte aligned");
+  if ((st = check_device()) != IRM_OK) return st;
+  return irm::launch_prefill_nonabsorbed(q_nope, q_rope, q_pos0, n_q, kv, kvh, kv_rows, n_heads, scale, out, lse,
+                                         static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
 // GQA/MHA comparison path
 // ---------------------------------------------------------------------------
 namespace {

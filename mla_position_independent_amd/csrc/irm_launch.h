@@ -37,6 +37,13 @@ irm_status launch_prefill_assembled(const void* q_lat, const void* q_rope, int32
                                     const void* kv, uint64_t kv_rows, uint32_t n_heads, float scale, void* out,
                                     float* lse, hipStream_t s);
 
+// irm_nonabsorbed.hip
+irm_status launch_kv_upproj(const void* kv, uint64_t kv_rows, const void* w_uk, const void* w_uv, uint32_t n_heads,
+                            void* out, hipStream_t s);
+irm_status launch_prefill_nonabsorbed(const void* q_nope, const void* q_rope, int32_t q_pos0, uint32_t n_q,
+                                      const void* kv, const void* kvh, uint64_t kv_rows, uint32_t n_heads,
+                                      float scale, void* out, float* lse, hipStream_t s);
+
 // Last pool row a kernel may touch (pool_rows is clamped to 2^32).
 inline uint32_t pool_last_of(uint64_t pool_rows) {
   return (uint32_t)((pool_rows < 0x100000000ull ? pool_rows : 0x100000000ull) - 1);

@@ -1,0 +1,371 @@
+// Non-absorbed MLA prefill: the latent rows of an assembled cache are
+// up-projected to a full key and value per head, then every head attends
+// with its own 192-wide key [k_nope | k_r] and 128-wide value (Irminsul
+// pages: gentlecold.top article, section 4 for the key [W_UK c_KV, k_r] and
+// the value from c_KV; section 13 for the non-absorbed form, which has to
+// up-project c_KV at run time).  k_r is the rotated slice of the assembled
+// row, shared by all heads; only it carries the position.
+//
+// Two kernels:
+//  * upproj_kernel: kvh[h][t] = [W_UK[h] c_KV[t] | W_UV[h] c_KV[t]] (bf16,
+//    256 per row and head), a [rows x 512] by [512 x 256] product per head on
+//    v_mfma_f32_16x16x32_bf16, both operands staged through LDS.
+//  * mha_prefill_kernel: causal attention of 128 queries of one head per
+//    workgroup over the head's rows, streamed in 32-row tiles through a
+//    three-stage LDS ring with one barrier per tile.
+
+#include <hip/hip_runtime.h>
+
+#include "irm_attn.h"
+#include "irm_launch.h"
+
+namespace irm {
+namespace {
+
+using namespace irm::dev;
+
+// LDS offset of 16-byte unit u of row r in a tile of 128-byte rows: units
+// are permuted by (r >> 1) & 7, so 16 lanes reading one unit of 16
+// consecutive rows cover all 64 banks.
+__device__ __forceinline__ uint32_t pos128(uint32_t r, uint32_t u) { return r * 128 + ((u ^ ((r >> 1) & 7)) << 4); }
+
+// ---------------------------------------------------------------------------
+// up-projection
+//
+// Workgroup = (head h, 128 rows), four waves; wave w computes features
+// 64w .. 64w+63 of the head's 256 (waves 0-1: W_UK, 2-3: W_UV) for all 128
+// rows, as D = W A^T: lane (q, r) ends with features 4q..4q+3 of a 16-feature
+// block for row r of a 16-row block, stored as 8 bytes.  The latent
+// dimension goes in 64-wide chunks through two LDS stages (kv rows 128 x 128
+// B, weights 256 x 128 B); within a chunk, MFMA step s takes units 4s + q.
+// ---------------------------------------------------------------------------
+constexpr int kUpRows = 128;
+constexpr int kUpFeat = 256;
+constexpr int kUpChunk = 64;                             // latent dims per stage
+constexpr int kUpChunks = IRM_D_LATENT / kUpChunk;      // 8
+constexpr int kUpA = kUpRows * 128;                      // 16 KB
+constexpr int kUpW = kUpFeat * 128;                      // 32 KB
+
+struct UpSmem {
+  unsigned char a[2][kUpA];
+  unsigned char w[2][kUpW];
+};
+
+struct UpArgs {
+  const unsigned char* kv;     // bf16 [rows][576]
+  const unsigned char* w_uk;   // bf16 [H][128][512]
+  const unsigned char* w_uv;   // bf16 [H][128][512]
+  unsigned char* out;          // bf16 [H][rows][256]
+  uint32_t rows, n_heads, row_tiles;
+};
+
+// Copies of chunk c into stage st: wave w moves kv rows 32w .. 32w+31 (4 KB)
+// and weight rows 64w .. 64w+63 (8 KB); lane l of a 1 KB copy fills row
+// base + l / 8, LDS position l % 8.
+__device__ __forceinline__ void up_issue(const UpArgs& a, UpSmem& sm, int st, uint32_t h, uint32_t m0, int c) {
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t p = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t r = 32 * w + 8 * i + (lane >> 3);
+    const uint32_t u = p ^ ((r >> 1) & 7);
+    const uint32_t row = min(m0 + r, a.rows - 1);
+    dma16(a.kv + (size_t)row * kRowBytes + c * 128 + 16 * u, lds_addr(sm.a[st] + (32 * w + 8 * i) * 128));
+  }
+  const unsigned char* wsrc = (w < 2 ? a.w_uk : a.w_uv) + (size_t)h * 128 * IRM_D_LATENT * 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t f = 64 * w + 8 * i + (lane >> 3);  // feature of the head, 0..255
+    const uint32_t u = p ^ ((f >> 1) & 7);
+    dma16(wsrc + (size_t)(f & 127) * IRM_D_LATENT * 2 + c * 128 + 16 * u,
+          lds_addr(sm.w[st] + (64 * w + 8 * i) * 128));
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void upproj_kernel(UpArgs a) {
+  __shared__ UpSmem sm;
+  const uint32_t b = blockIdx.x;
+  const uint32_t h = b % a.n_heads, m0 = (b / a.n_heads) * kUpRows;
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t q = lane >> 4, r = lane & 15;
+
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  up_issue(a, sm, 0, h, m0, 0);
+  for (int c = 0; c < kUpChunks; ++c) {
+    const int st = c & 1;
+    wait_dma_all();
+    __syncthreads();  // chunk c is in LDS; every wave is done with chunk c - 1
+    if (c + 1 < kUpChunks) up_issue(a, sm, st ^ 1, h, m0, c + 1);
+    const unsigned char* A = sm.a[st];
+    const unsigned char* W = sm.w[st];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t u = 4 * s + q;
+      bf16x8_t wf[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        wf[nb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(W + pos128(64 * w + 16 * nb + r, u)));
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(A + pos128(16 * mb + r, u)));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nb], af, acc[nb][mb], 0, 0, 0);
+      }
+    }
+  }
+  // lane (q, r): features 64w + 16nb + 4q .. +3 of row m0 + 16mb + r
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const uint32_t m = m0 + 16 * mb + r;
+    if (m >= a.rows) continue;
+    unsigned char* dst = a.out + ((size_t)h * a.rows + m) * (kUpFeat * 2) + (64 * w + 4 * q) * 2;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x4_t& v = acc[nb][mb];
+      *reinterpret_cast<uint2*>(dst + 32 * nb) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-head causal prefill
+//
+// Workgroup = (head h, 128 queries); wave w owns queries 32w .. 32w+31 as two
+// 16-query blocks and walks every tile of the keys they can see.  Scores are
+// S^T = K Q^T (lane (q, r): keys 4q..4q+3 of a 16-key block for query r);
+// with two key blocks per tile each lane holds 8 scores per query block, the
+// shape of the shared branch-free online softmax.  O^T = V^T P^T leaves
+// every lane with value dims 4q..4q+3 of one query, so the rescale is
+// lane-local.
+//
+// Stage (32 keys, 20 KB): k_nope [32][256 B] (unit c of row r at c ^ (r & 15)),
+// k_r [32][128 B] (pos128), v [32][256 B] (as k_nope).  Wave w copies rows
+// 8w .. 8w+7 of each part: five 1 KB LDS-DMA copies per tile.
+// ---------------------------------------------------------------------------
+constexpr int kMhaQ = 128;                 // queries per workgroup
+constexpr int kMhaT = 32;                  // keys per tile
+constexpr int kMhaStages = 3;
+constexpr int kMhaKn = kMhaT * 256;        // 8 KB
+constexpr int kMhaKr = kMhaT * 128;        // 4 KB
+constexpr int kMhaStage = 2 * kMhaKn + kMhaKr;
+constexpr int kMhaCopies = 5;              // LDS-DMA copies per wave and tile
+
+struct MhaSmem {
+  unsigned char st[kMhaStages][kMhaStage];
+};
+
+struct MhaArgs {
+  const unsigned char* q_nope;  // bf16 [n_q][H][128]
+  const unsigned char* q_rope;  // bf16 [n_q][H][64]
+  const unsigned char* kv;      // bf16 [rows][576] (k_r at byte 1024)
+  const unsigned char* kvh;     // bf16 [H][rows][256] = [k_nope | v]
+  unsigned char* out;           // bf16 [n_q][H][128]
+  float* lse;                   // [n_q][H] or null
+  uint32_t rows, n_heads, n_q, q_blocks;
+  int32_t q_pos0;
+  float c;                      // scale * log2(e)
+};
+
+__device__ __forceinline__ void mha_issue(const MhaArgs& a, unsigned char* st, uint32_t h, uint32_t t0) {
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const unsigned char* head = a.kvh + (size_t)h * a.rows * 512;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t r = 8 * w + 4 * i + (lane >> 4);
+    const uint32_t u = (lane & 15) ^ (r & 15);
+    const unsigned char* src = head + (size_t)min(t0 + r, a.rows - 1) * 512 + 16 * u;
+    dma16(src, lds_addr(st + (8 * w + 4 * i) * 256));                   // k_nope
+    dma16(src + 256, lds_addr(st + kMhaKn + kMhaKr + (8 * w + 4 * i) * 256));  // v
+  }
+  const uint32_t r = 8 * w + (lane >> 3);
+  const uint32_t u = (lane & 7) ^ ((r >> 1) & 7);
+  dma16(a.kv + (size_t)min(t0 + r, a.rows - 1) * kRowBytes + kCkvBytes + 16 * u, lds_addr(st + kMhaKn + 8 * w * 128));
+}
+
+// Transposing reads of V^T (see ct_bases in irm_attn.h, here on 256-byte
+// rows): lane (q, s) reads row R0 + x, x = 4q + s/4, 8 bytes of unit 2nb + hh,
+// hh = (s % 4) / 2, which sits at position (2nb + hh) ^ x.
+__device__ __forceinline__ void v_bases(const unsigned char* v, const unsigned char* (&b)[8]) {
+  const uint32_t lane = opaque(threadIdx.x & 63), q = lane >> 4, s = lane & 15;
+  const uint32_t x = 4 * q + (s >> 2);
+  const uint32_t hh = (s & 3) >> 1;
+  const unsigned char* rowp = v + x * 256 + ((hh ^ (x & 1)) << 4) + 8 * (s & 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = rowp + (((uint32_t)i ^ (x >> 1)) << 5);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void mha_prefill_kernel(MhaArgs a) {
+  __shared__ MhaSmem sm;
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const uint32_t h = blockIdx.x % a.n_heads;
+  const uint32_t qblk = a.q_blocks - 1 - blockIdx.x / a.n_heads;  // longest blocks first
+  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t q = lane >> 4, r = lane & 15;
+  const uint32_t qw = qblk * kMhaQ + 32 * w;                     // first query of the wave
+  const uint32_t q_last = min(qblk * kMhaQ + kMhaQ, a.n_q) - 1;  // last valid query of the workgroup
+  const uint32_t n_keys = (uint32_t)a.q_pos0 + q_last + 1;
+  const uint32_t n_tiles = (n_keys + kMhaT - 1) / kMhaT;
+
+  // Q^T operands: block b, step kk (0-3 nope, 4-5 rope), lane (q, r) holds
+  // dims 32kk + 8q .. +8 of query qw + 16b + r (clamped past the last query)
+  bf16x8_t qf[2][6];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t qi = min(qw + 16 * b + r, a.n_q - 1);
+    const uint4* pn = reinterpret_cast<const uint4*>(a.q_nope + ((size_t)qi * a.n_heads + h) * 256) + q;
+    const uint4* pr = reinterpret_cast<const uint4*>(a.q_rope + ((size_t)qi * a.n_heads + h) * 128) + q;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[b][kk] = __builtin_bit_cast(bf16x8_t, pn[4 * kk]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) qf[b][4 + kk] = __builtin_bit_cast(bf16x8_t, pr[4 * kk]);
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) asm volatile("" : "+v"(qf[b][kk]));
+
+  f32x4_t o[8][2];
+#pragma unroll
+  for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) o[vb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  // a query at position q_pos0 + i sees keys t <= q_pos0 + i
+  const int32_t lim0 = a.q_pos0 + (int32_t)(qw + r), lim1 = lim0 + 16;
+  const uint32_t first_masked = (uint32_t)a.q_pos0 + qw + 1;  // tiles ending at or below this need no mask
+
+  mha_issue(a, sm.st[0], h, 0);
+  if (n_tiles > 1) mha_issue(a, sm.st[1], h, kMhaT);
+  for (uint32_t t = 0; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kMhaCopies) : "memory");
+    else
+      wait_dma_all();
+    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
+    if (t + 2 < n_tiles) mha_issue(a, sm.st[(t + 2) % kMhaStages], h, (t + 2) * kMhaT);
+    const unsigned char* st = sm.st[t % kMhaStages];
+    const unsigned char* kn = st;
+    const unsigned char* kr = st + kMhaKn;
+    const unsigned char* v = st + kMhaKn + kMhaKr;
+
+    // scores: S^T of key blocks j = 0, 1 for query blocks b = 0, 1
+    f32x4_t s[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) s[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t rr = opaque(r);
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) {
+      bf16x8_t kf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t row = 16 * j + rr;
+        const unsigned char* p = kk < 4 ? kn + row * 256 + (((4 * kk + q) ^ rr) << 4) : kr + pos128(row, 4 * (kk - 4) + q);
+        kf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[b][kk], s[b][j], 0, 0, 0);
+    }
+
+    // online softmax per query block; the causal mask only near the diagonal
+    const uint32_t t0 = t * kMhaT;
+    const bool masked = t0 + kMhaT > first_masked;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float sv[2][4], p[2][4], alpha;
+      const int32_t lim = b ? lim1 : lim0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t key = (int32_t)(t0 + 16 * j + 4 * q + i);
+          sv[j][i] = (masked && key > lim) ? -INFINITY : s[b][j][i];
+        }
+      if (softmax_scores(sv, a.c, m[b], l[b], p, alpha)) {
+#pragma unroll
+        for (int vb = 0; vb < 8; ++vb) o[vb][b] *= alpha;
+      }
+      pb[b] = pack_p8(p[0], p[1]);
+    }
+
+    // O^T += V^T P^T: keys {4q..4q+3, 16+4q..16+4q+3} in the lane's k order
+    const unsigned char* vb8[8];
+    v_bases(v, vb8);
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)vb8[vb]);
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vb8[vb] + 16 * 256));
+      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+      for (int b = 0; b < 2; ++b) o[vb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[b], o[vb][b], 0, 0, 0);
+    }
+  }
+
+  // normalise and store: lane (q, r) holds value dims 16vb + 4q .. +3 of query qw + 16b + r
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float lt = l[b];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const uint32_t qi = qw + 16 * b + r;
+    if (qi >= a.n_q) continue;
+    const float inv = 1.f / lt;
+    unsigned char* dst = a.out + ((size_t)qi * a.n_heads + h) * 256 + 8 * q;
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) {
+      const f32x4_t& x = o[vb][b];
+      *reinterpret_cast<uint2*>(dst + 32 * vb) =
+          make_uint2(pack_bf16(x[0] * inv, x[1] * inv), pack_bf16(x[2] * inv, x[3] * inv));
+    }
+    if (a.lse && q == 0) a.lse[(size_t)qi * a.n_heads + h] = (m[b] + __log2f(lt)) * kLn2;
+  }
+}
+
+}  // namespace
+
+irm_status launch_kv_upproj(const void* kv, uint64_t kv_rows, const void* w_uk, const void* w_uv, uint32_t n_heads,
+                            void* out, hipStream_t s) {
+  if (!kv_rows) return IRM_OK;
+  UpArgs a;
+  a.kv = static_cast<const unsigned char*>(kv);
+  a.w_uk = static_cast<const unsigned char*>(w_uk);
+  a.w_uv = static_cast<const unsigned char*>(w_uv);
+  a.out = static_cast<unsigned char*>(out);
+  a.rows = (uint32_t)kv_rows;
+  a.n_heads = n_heads;
+  a.row_tiles = (uint32_t)((kv_rows + kUpRows - 1) / kUpRows);
+  hipLaunchKernelGGL(upproj_kernel, dim3(a.row_tiles * n_heads), dim3(kThreads), 0, s, a);
+  return launch_check("up-projection kernel");
+}
+
+irm_status launch_prefill_nonabsorbed(const void* q_nope, const void* q_rope, int32_t q_pos0, uint32_t n_q,
+                                      const void* kv, const void* kvh, uint64_t kv_rows, uint32_t n_heads,
+                                      float scale, void* out, float* lse, hipStream_t s) {
+  MhaArgs a;
+  a.q_nope = static_cast<const unsigned char*>(q_nope);
+  a.q_rope = static_cast<const unsigned char*>(q_rope);
+  a.kv = static_cast<const unsigned char*>(kv);
+  a.kvh = static_cast<const unsigned char*>(kvh);
+  a.out = static_cast<unsigned char*>(out);
+  a.lse = lse;
+  a.rows = (uint32_t)kv_rows;
+  a.n_heads = n_heads;
+  a.n_q = n_q;
+  a.q_blocks = (n_q + kMhaQ - 1) / kMhaQ;
+  a.q_pos0 = q_pos0;
+  a.c = scale * kLog2e;
+  hipLaunchKernelGGL(mha_prefill_kernel, dim3(a.q_blocks * n_heads), dim3(kThreads), 0, s, a);
+  return launch_check("non-absorbed prefill kernel");
+}
+
+}  // namespace irm

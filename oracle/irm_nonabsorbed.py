@@ -31,9 +31,9 @@ def up_project(c_kv: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray) -> Tuple[np
     """k_nope[t][h] = W_UK[h] c_KV[t], v[t][h] = W_UV[h] c_KV[t] (float64).
     c_kv [N][512], w_uk / w_uv [H][128][512].  Returns ([N][H][128], [N][H][128])."""
     c = np.asarray(c_kv, dtype=np.float64)
-    k = np.einsum("hjc,tc->thj", np.asarray(w_uk, dtype=np.float64), c)
-    v = np.einsum("hjc,tc->thj", np.asarray(w_uv, dtype=np.float64), c)
-    return k, v
+    k = np.matmul(c, np.asarray(w_uk, dtype=np.float64).transpose(0, 2, 1))   # [H][N][128]
+    v = np.matmul(c, np.asarray(w_uv, dtype=np.float64).transpose(0, 2, 1))
+    return np.ascontiguousarray(k.transpose(1, 0, 2)), np.ascontiguousarray(v.transpose(1, 0, 2))
 
 
 def _attend(s: np.ndarray, values: np.ndarray) -> Tuple[np.ndarray, float]:

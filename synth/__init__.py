@@ -22,5 +22,6 @@ from .workloads import (  # noqa: F401
     long_decode,
     tail_prefill,
     token_requests,
+    nonabsorbed_inputs,
     manifest,
 )

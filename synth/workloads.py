@@ -176,6 +176,18 @@ def _queries(rng, n: int, h: int) -> Tuple[np.ndarray, np.ndarray]:
     return q_lat, q_rope
 
 
+def nonabsorbed_inputs(seed: int, n_q: int, heads: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Random up-projection weights and nope queries of the non-absorbed MLA
+    prefill (no trained weights): q_nope [n_q][H][128] N(0,1), W_UK and W_UV
+    [H][128][512] N(0, 1/512) (so that W c_KV is about unit scale for N(0,1)
+    latents), all rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    q_nope = randn_bf16(rng, (n_q, heads, 128))
+    w = rng.standard_normal((2, heads, 128, D_LATENT), dtype=np.float32) * np.float32(1.0 / np.sqrt(D_LATENT))
+    w_bits = bf16_bits_from_f32(w)
+    return q_nope, w_bits[0], w_bits[1]
+
+
 # --------------------------------------------------------------------------
 # the five workloads of the hot path
 # --------------------------------------------------------------------------

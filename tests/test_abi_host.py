@@ -144,3 +144,24 @@ def test_prefill_assembled_validation_errors():
     assert st(kv=A + 8) == "EINVAL"
     assert st(out=A + 2) == "EINVAL"
 
+
+def test_nonabsorbed_validation_errors():
+    """Argument checks of irm_mla_kv_upproj and irm_mla_prefill_nonabsorbed
+    come before any HIP call."""
+    import ctypes
+    L = irm.lib()
+    A = 4096
+    def up(kv=A, rows=64, w=A, heads=16, out=A):
+        return irm.STATUS[L.irm_mla_kv_upproj(kv, rows, w, w, heads, out, None)]
+    assert up(heads=0) == "EUNSUPPORTED" and up(heads=129) == "EUNSUPPORTED"
+    assert up(rows=2**32) == "EUNSUPPORTED"
+    assert up(kv=None) == "EINVAL" and up(w=A + 4) == "EINVAL" and up(out=A + 8) == "EINVAL"
+    def pf(q_pos0=0, n_q=1, kv=A, kvh=A, rows=64, heads=16, scale=0.1, q=A, out=A):
+        return irm.STATUS[L.irm_mla_prefill_nonabsorbed(q, q, q_pos0, n_q, kv, kvh, rows, heads,
+                                                        ctypes.c_float(scale), out, None, None)]
+    assert pf(heads=0) == "EUNSUPPORTED" and pf(heads=200) == "EUNSUPPORTED"
+    assert pf(rows=2**32) == "EUNSUPPORTED"
+    assert pf(scale=float("inf")) == "EINVAL" and pf(scale=-1.0) == "EINVAL"
+    assert pf(q_pos0=-1) == "ERANGE" and pf(n_q=0) == "ERANGE" and pf(q_pos0=60, n_q=5) == "ERANGE"
+    assert pf(kvh=None) == "EINVAL" and pf(kv=A + 2) == "EINVAL" and pf(q=A + 8) == "EINVAL"
+

@@ -18,7 +18,8 @@ import pytest
 import mla_position_independent_amd as irm
 import oracle
 from synth import (CHUNK_DTYPE, FRESH, random_table, tiny_decode, rotate_gather_batch,
-                   batched_decode, long_decode, tail_prefill)
+                   batched_decode, long_decode, tail_prefill, nonabsorbed_inputs)
+from oracle import irm_nonabsorbed as NA
 
 pytestmark = pytest.mark.gpu
 
@@ -495,6 +496,105 @@ def test_prefill_full_size_sampled():
     o, l = _gpu_prefill(w)
     qids = [0, 1, 2047, 4094, 4095]
     o_ref, l_ref = _oracle_prefill(w, qids)
+    assert rel_l2(o[qids], o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
+    assert np.all(np.isfinite(o))
+
+
+# ---------------------------------------------------------------- non-absorbed prefill
+def _upproj_bound(c, w):
+    """|bf16(float sum) - exact| <= one bf16 ulp of the exact value (RNE, with
+    slack) + 2^-15 sum |c w| (any order of 512 float additions of exact bf16
+    products: n u with n = 2^9, u = 2^-24)."""
+    return lambda exact, h: _bf16_ulp(exact) * 1.0000001 + 2.0 ** -15 * (np.abs(c) @ np.abs(w[h]).T)
+
+
+@pytest.mark.parametrize("seed,rows,heads", [(61, 1, 1), (62, 130, 3), (63, 700, 16), (64, 256, 128)])
+def test_kv_upproj(seed, rows, heads):
+    rng = np.random.default_rng(seed)
+    from synth import randn_bf16
+    kv_bits = randn_bf16(rng, (rows, 576))
+    _, wk, wv = nonabsorbed_inputs(seed, 1, heads)
+    got = irm.from_device_bf16(irm.mla_kv_upproj(irm.to_device_bf16(kv_bits), irm.to_device_bf16(wk),
+                                                 irm.to_device_bf16(wv)))
+    _sync()
+    c = oracle.bf16_to_f64(kv_bits[:, :512])
+    k, v = NA.up_project(c, oracle.bf16_to_f64(wk), oracle.bf16_to_f64(wv))
+    g = oracle.bf16_to_f64(got)                                  # [H][rows][256]
+    for h in range(heads):
+        for part, exact, w in ((slice(0, 128), k[:, h], wk), (slice(128, 256), v[:, h], wv)):
+            bound = _upproj_bound(c, oracle.bf16_to_f64(w))(exact, h)
+            assert np.all(np.abs(g[h][:, part] - exact) <= bound), (h, part)
+
+
+def _na_case(w, seed):
+    q_nope, wk, wv = nonabsorbed_inputs(seed, w.q_lat.shape[0], w.n_heads)
+    return q_nope, wk, wv
+
+
+def _gpu_nonabsorbed(w, q_nope, wk, wv, q_scale=1.0):
+    import torch
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    kv = irm.rotate_gather(t, pool)
+    kvh = irm.mla_kv_upproj(kv, irm.to_device_bf16(wk), irm.to_device_bf16(wv))
+    qn = irm.to_device_bf16(q_nope)
+    qr = irm.to_device_bf16(w.q_rope)
+    if q_scale != 1.0:
+        qn = (qn.float() * q_scale).to(torch.bfloat16)
+        qr = (qr.float() * q_scale).to(torch.bfloat16)
+    out, lse = irm.mla_prefill_nonabsorbed(qn, qr, w.q_pos0, kv, kvh, scale=w.scale, want_lse=True)
+    _sync()
+    return (oracle.bf16_to_f64(irm.from_device_bf16(out)), lse.cpu().numpy().astype(np.float64),
+            oracle.bf16_to_f64(irm.from_device_bf16(qn)), oracle.bf16_to_f64(irm.from_device_bf16(qr)))
+
+
+def _oracle_nonabsorbed(w, qn, qr, wk, wv, qids):
+    inv = oracle.rope_inv_freq(w.theta)
+    (g, d, _), = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
+    c, k = oracle.assemble_rows(w.pool, g, d, inv)
+    return NA.mla_prefill_nonabsorbed(qn, qr, c, k, oracle.bf16_to_f64(wk), oracle.bf16_to_f64(wv), w.q_pos0,
+                                      w.scale, query_ids=qids)
+
+
+@pytest.mark.parametrize("seed,heads,N,nq", [
+    (71, 16, 700, 130), (72, 1, 333, 1), (73, 3, 64, 64), (74, 16, 95, 33), (75, 128, 520, 9), (76, 2, 300, 257),
+])
+def test_prefill_nonabsorbed_random(seed, heads, N, nq):
+    """Assemble (rotate-gather), up-project, attend; against the oracle on the
+    exact assembled rows.  Besides the bf16 rounding of the rotated k_r, the
+    kernels round k_nope and v to bf16 (the stored per-head cache), which
+    moves a score by about scale * 2^-9 |q_nope| |k_nope| / sqrt(3) and the
+    output by a softmax mean of 2^-9 relative errors: well inside the bar."""
+    w = random_table(seed, [N], heads=heads, p_hit=0.7, prefix_frac=0.25, n_q=nq, kind="prefill")
+    q_nope, wk, wv = _na_case(w, seed)
+    o, l, qn, qr = _gpu_nonabsorbed(w, q_nope, wk, wv)
+    o_ref, l_ref = _oracle_nonabsorbed(w, qn, qr, wk, wv, None)
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= LSE_TOL
+    for i in (0, nq - 1):
+        assert rel_l2(o[i], o_ref[i]) <= ATTN_TOL
+
+
+def test_prefill_nonabsorbed_rescale():
+    """Queries times 4: scores spread far wider, so the running maximum moves
+    often and the rescale of O runs; lse tolerance scaled like the score error."""
+    w = random_table(77, [900], heads=16, p_hit=0.9, len_fn=_tiny_chunks, n_q=70, kind="prefill")
+    q_nope, wk, wv = _na_case(w, 77)
+    o, l, qn, qr = _gpu_nonabsorbed(w, q_nope, wk, wv, q_scale=4.0)
+    o_ref, l_ref = _oracle_nonabsorbed(w, qn, qr, wk, wv, None)
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= 4.0 * LSE_TOL
+
+
+def test_prefill_nonabsorbed_full_size_sampled():
+    """The benchmarked shape: 4096 queries at 61440.. over 65536 assembled
+    rows, 16 heads, compared on sampled queries."""
+    w = tail_prefill()
+    q_nope, wk, wv = _na_case(w, 1005)
+    o, l, qn, qr = _gpu_nonabsorbed(w, q_nope, wk, wv)
+    qids = [0, 1, 127, 128, 2047, 4095]
+    o_ref, l_ref = _oracle_nonabsorbed(w, qn, qr, wk, wv, qids)
     assert rel_l2(o[qids], o_ref) <= ATTN_TOL
     assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
     assert np.all(np.isfinite(o))
