@@ -220,7 +220,7 @@ def leg_decode(args, irm, torch, synth, name, make):
     }
 
 
-def leg_prefill(args, irm, torch, synth):
+def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = True):
     """One call = assemble the 65536-row cache with rotate-gather, then the
     causal prefill of the 4096 queries over it (irm_mla_prefill_assembled).
     The roofline is the prefill kernel's own time (events around it); the
@@ -243,7 +243,7 @@ def leg_prefill(args, irm, torch, synth):
         if ev is not None:
             ev[1].record()
 
-    def fused(ev):
+    def fused_call(ev):
         if ev is not None:
             ev[0].record()
         irm.mla_prefill_tail(ql, qr, w.q_pos0, t, pool, scale=w.scale, out=out)
@@ -251,17 +251,23 @@ def leg_prefill(args, irm, torch, synth):
             ev[1].record()
 
     n_steps, n_warm = max(2, args.steps // 4), min(args.warmup, 2)
+    if not assembled:   # profiling the fused kernel alone
+        _, fused_ms = time_leg(fused_call, n_steps, n_warm)
+        log(f"tail-prefill, rotation on load in one kernel: {fused_ms:.3f} ms")
+        return None
     ms, kern_ms = time_leg(step, n_steps, n_warm)
-    _, fused_ms = time_leg(fused, n_steps, 1)
+    fused_ms = time_leg(fused_call, n_steps, 1)[1] if fused else None
     pairs = nq * w.q_pos0 + nq * (nq + 1) // 2      # visible (query, key) pairs
     flops = pairs * H * 2 * (576 + 512)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     log(f"tail-prefill: {ms:.3f} ms/call (rotate-gather + prefill over the assembled cache; prefill kernel "
-        f"{kern_ms:.3f} ms, {achieved:.0f} TFLOP/s); rotation on load in one kernel: {fused_ms:.3f} ms")
+        f"{kern_ms:.3f} ms, {achieved:.0f} TFLOP/s); rotation on load in one kernel: "
+        + ("not timed" if fused_ms is None else f"{fused_ms:.3f} ms"))
     return {
         "workload": w.name, "ms_per_call": round(ms, 4), "queries": nq, "kv_rows": t.total_rows,
         "call": "irm_rotate_gather + irm_mla_prefill_assembled",
-        "prefill_kernel_ms": round(kern_ms, 4), "fused_rotate_on_load_ms": round(fused_ms, 4),
+        "prefill_kernel_ms": round(kern_ms, 4),
+        "fused_rotate_on_load_ms": None if fused_ms is None else round(fused_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
                      "traffic": measured_traffic("prefill_kernel"), "kernel": "prefill_kernel (assembled cache)",
@@ -501,8 +507,10 @@ def main():
                 leg_decode(args, irm, torch, synth, "batched decode", synth.batched_decode)
             elif name == "long_decode":
                 leg_decode(args, irm, torch, synth, "long decode", synth.long_decode)
-            elif name == "prefill":
-                leg_prefill(args, irm, torch, synth)
+            elif name == "prefill":        # the assembled-cache pair only (one prefill instantiation)
+                leg_prefill(args, irm, torch, synth, fused=False)
+            elif name == "prefill_fused":  # the single kernel with rotation on load only
+                leg_prefill(args, irm, torch, synth, assembled=False)
             elif name == "producer":
                 leg_producer(args, irm, synth, 0.0)
             elif name == "nonabsorbed":
