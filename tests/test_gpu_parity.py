@@ -628,6 +628,63 @@ def test_error_paths():
     assert e.value.code == "EWORKSPACE"
 
 
+def test_decode_workspace_random_contents():
+    """Random bytes in the workspace change nothing: every split slot is
+    written before the combine pass reads it."""
+    import torch
+    w = random_table(14, [2000, 700, 64, 3000], heads=32)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    outs = []
+    for seed, S in ((1, 4), (2, 4), (3, 7)):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        ws = torch.randint(0, 256, (irm.decode_workspace_bytes(t, w.n_heads, S),), dtype=torch.uint8,
+                           device="cuda", generator=gen)
+        out, lse = irm.mla_decode(ql, qr, t, pool, n_splits=S, scale=w.scale, want_lse=True, workspace=ws)
+        _sync()
+        o = oracle.bf16_to_f64(irm.from_device_bf16(out))
+        assert rel_l2(o, o_ref) <= ATTN_TOL and np.max(np.abs(lse.cpu().numpy() - l_ref)) <= LSE_TOL
+        outs.append(o)
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_decode_graph_replay():
+    """A decode captured in a HIP graph and replayed (with eager decodes on the
+    same workspace in between, and new query values) matches the eager call
+    bit for bit on every replay."""
+    import torch
+    w = random_table(15, [1500, 900, 2600], heads=16)
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    ws = torch.zeros(irm.decode_workspace_bytes(t, 16, 4), dtype=torch.uint8, device="cuda")
+    out_g = torch.empty((w.n_seq, 16, 512), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        irm.mla_decode(ql, qr, t, pool, n_splits=4, scale=w.scale, out=out_g, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        irm.mla_decode(ql, qr, t, pool, n_splits=4, scale=w.scale, out=out_g, workspace=ws)
+    rng = np.random.default_rng(16)
+    for rep in range(4):
+        if rep >= 2:   # new queries in the captured input buffers
+            from synth import randn_bf16
+            ql.copy_(irm.to_device_bf16(randn_bf16(rng, tuple(ql.shape))))
+            qr.copy_(irm.to_device_bf16(randn_bf16(rng, tuple(qr.shape))))
+        graph.replay()
+        _sync()
+        got = irm.from_device_bf16(out_g).copy()
+        eager = irm.mla_decode(ql, qr, t, pool, n_splits=4, scale=w.scale, workspace=ws)
+        _sync()
+        assert np.array_equal(got, irm.from_device_bf16(eager)), rep
+
+
 def test_decode_workspace_reuse_across_split_counts():
     """One workspace serves consecutive decodes with different split counts;
     no call may depend on what an earlier call left in it."""
