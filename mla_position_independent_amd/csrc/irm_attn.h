@@ -649,7 +649,9 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
         x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ptr));
       }
     };
-    constexpr int kAhead = 8;
+    // K fragments read ahead of their MFMAs: a shallow ring keeps the LDS queue
+    // short for the accumulating waves (2 to 3 measured 5% faster than 8)
+    constexpr int kAhead = 2;
     bf16x8_t ring[kAhead + 1][2];
 #pragma unroll
     for (int kk = 0; kk < kAhead; ++kk) read(kk, ring[kk]);
@@ -773,7 +775,7 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
             (lds_i16x4_ptr)(c0.b[nn & 7] + 256 * (nn >> 3) + 16 * kCkvBytes));
         return __builtin_bit_cast(bf16x8_t, (i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
       };
-      constexpr int kCfAhead = 4;  // C^T fragments in registers at a time
+      constexpr int kCfAhead = 3;  // C^T fragments in registers at a time
       bf16x8_t cf[kCfAhead];
 #pragma unroll
       for (int nb = 0; nb < kCfAhead; ++nb) cf[nb] = read_cf(nb);
