@@ -68,6 +68,7 @@ __device__ __forceinline__ uint32_t kr_pos(uint32_t r, uint32_t u) {
 struct StreamArgs {
   const unsigned char* pool;
   const uint4* rowmap;  // padded by kTile records past the last row
+  const float2* trig;   // (cos, sin) of every entry's delta, [n_entries][32]
   uint32_t pool_last;
 };
 
@@ -368,6 +369,27 @@ __device__ __forceinline__ int32_t slice_row_delta(const uint4* rec) {
   return (int32_t)rec[(threadIdx.x & 63) / (64 / R)].y;
 }
 
+// Fill the wave's trig table with the precomputed (cos, sin) rows of the
+// entries of two slice rows, the first and the last with a nonzero delta
+// (lane l holds delta d of its row, rec the slice's row-map records): lanes
+// 0..15 copy the first entry's 256 bytes into slot 0, lanes 16..31 the last
+// one's into slot 1, and cd takes the two deltas.  Does nothing when the
+// table already holds every nonzero delta of the slice (most slices), so a
+// copy goes out only at entry boundaries; callers' waits count only copies
+// issued after it.
+template <int kSlots, int R>
+__device__ __forceinline__ void slice_trig_fetch(const StreamArgs& ra, WaveSlots<kSlots, R>& ws, int32_t d,
+                                                 const uint4* rec, int32_t (&cd)[2]) {
+  if (!__any(d != 0 && d != cd[0] && d != cd[1])) return;
+  const uint32_t l = threadIdx.x & 63;
+  const uint64_t nz = __ballot(d != 0);
+  const int first = __ffsll((unsigned long long)nz) - 1, last = 63 - __clzll((long long)nz);
+  cd[0] = __shfl(d, first);
+  cd[1] = __shfl(d, last);
+  const uint32_t ent = rec[(uint32_t)((l < 16) ? first : last) / (64 / R)].z;
+  if (l < 32) dma16(ra.trig + (size_t)ent * kPairs + 2 * (l & 15), lds_addr(&ws.trig[0][0]));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_dma_but() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
@@ -506,31 +528,6 @@ __device__ __forceinline__ void copy_kr(const StreamArgs& ra, const SliceCopies&
   const uint32_t l = threadIdx.x & 63, r = row0 + (l >> 3);
   dma16(ra.pool + (size_t)cp.ksrc * kRowBytes + kCkvBytes + (((l & 7) ^ ((r >> 1) & 7)) << 4),
         lds_addr(kr + row0 * kKrBytes));
-}
-
-// Make the wave's trig table hold the delta of every row of the slice
-// (lane l: row l / 8, delta d).  Returns false if the slice holds more
-// distinct nonzero deltas than the table (two); the caller then rotates with
-// slice_rotate, which handles any number.
-template <int kSlots>
-__device__ __forceinline__ bool slice_trig_ready(WaveSlots<kSlots, kTileSlice>& ws, const double* omega, int32_t d,
-                                                 int32_t (&cd)[2]) {
-  const uint32_t l = threadIdx.x & 63;
-  if (!__any(d != 0 && d != cd[0] && d != cd[1])) return true;
-  const uint64_t nz = __ballot(d != 0);
-  cd[0] = __shfl(d, __ffsll((unsigned long long)nz) - 1);
-  cd[1] = __shfl(d, 63 - __clzll((long long)nz));
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  {
-    double sn, cn;
-    sincos((double)cd[l >> 5] * omega[l & 31], &sn, &cn);
-    ws.trig[l >> 5][l & 31] = make_float2((float)cn, (float)sn);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  return !__any(d != 0 && d != cd[0] && d != cd[1]);
 }
 
 // Rotation of the slice's k_r from the table in two halves, so that the
@@ -742,23 +739,29 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
     unsigned char* nx = stage(t + 2);
     unsigned char* sr = stage(t + 1) + kTileKr;
     // Tile t+1 needs turning unless every row of the slice has delta 0
-    // (exact-prefix and fresh rows, or a slice past the end).
+    // (exact-prefix and fresh rows, or a slice past the end).  The trig
+    // table holds the rows of the slice's first and last rotated entries
+    // (cd), copied one iteration earlier; a slice with a third delta (entries
+    // shorter than 8 rows) is turned by slice_rotate, which evaluates the
+    // missing deltas in double.
     const bool rot = t + 1 < nt && __any(d1 != 0);
-    const bool table = rot && slice_trig_ready(ws, sm.s.omega, d1, cd);
-    // Tile t+1 has landed: after its copies only the row map of tile t+3
-    // went out (t >= 1); at t = 0 nothing did.
+    const bool table = rot && !__any(d1 != 0 && d1 != cd[0] && d1 != cd[1]);
+    // Tile t+1 and its trig rows have landed: after them only the row map of
+    // tile t+3 went out (t >= 1); at t = 0 nothing did.
     wait_dma_but<B ? kRowMaps : 0>();
+    if (rot && !table) slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d1, cd);
     SliceRot rt;
     if (table) rt = slice_rot_load(ws, sr, row0, d1, cd);
-    const int32_t d_rot = d1;
     copy_kr(ra, cp, nx + kTileKr, row0);
     auto mid = [&]() {
+      // the table's reads are done once the rotated values are stored
       if (table) slice_rot_store(sr, row0, rt);
       // This iteration's copies of tile t+2 are out; the row map of tile
       // t+3, issued before them, has landed.
       if constexpr (!kFlat) wait_dma_but<kTileSlice - kScoreRows + 1>();
       cp = copies_of(t + 3);
       d1 = delta(t + 2);
+      if constexpr (!kFlat) slice_trig_fetch(ra, ws, d1, ws.rm[(t + 2) % kTileRm], cd);
     };
     if constexpr (B) {
       const uint32_t pb = (t - 1) & 1;
@@ -806,7 +809,6 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
       mid();
     }
     if constexpr (!kFlat) slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);
-    if (rot && !table) slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d_rot, cd);
     if constexpr (B) {
       if (seg_tiles && (t % seg_tiles == 0 || t == nt)) {  // tile t-1 closed a segment
         seg_end((t - 1) / seg_tiles, o);
@@ -833,6 +835,7 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
   d1 = delta(1);
   wait_dma_but<kTileSlice + 1>();  // tile 0 has landed (tile 1's copies may be outstanding)
   slice_rotate<kTileSlice>(ws, stage(0) + kTileKr, row0, sm.s.omega, delta(0), cd);
+  if constexpr (!kFlat) slice_trig_fetch(ra, ws, d1, ws.rm[1], cd);  // trig rows of tile 1
   __syncthreads();
   iteration(0, std::false_type{});
   for (uint32_t t = 1; t <= nt; ++t) iteration(t, std::true_type{});

@@ -49,20 +49,6 @@ __device__ __forceinline__ void mask_rows(const f32x4_t& acc, uint32_t row0, uin
   for (int i = 0; i < 4; ++i) sc[i] = (row0 + 4 * hq + i < nvalid) ? acc[i] : -INFINITY;
 }
 
-// Write one wave's softmax state for its 16 heads (lane (hq, hr) holds head
-// hr, columns 16 nb + 4 hq + i) into the split's workspace slot.
-__device__ __forceinline__ void store_partial(const DecodeArgs& a, size_t pidx, float m, float l, const f32x4_t (&o)[32]) {
-  const uint32_t lane = threadIdx.x & 63, hq = lane >> 4, hr = lane & 15;
-  float* dst = a.ws_acc + (pidx + hr) * IRM_D_LATENT + 4 * hq;
-#pragma unroll
-  for (int nb = 0; nb < 32; ++nb)
-    *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[nb][0], o[nb][1], o[nb][2], o[nb][3]);
-  if (hq == 0) {
-    a.ws_ml[(pidx + hr) * 2 + 0] = m;
-    a.ws_ml[(pidx + hr) * 2 + 1] = (m == -INFINITY) ? 0.f : l;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // split-KV decode, pass 1, one 16-head group per workgroup: wave-private
 // streams
@@ -342,6 +328,7 @@ StreamArgs stream_args(const irm_table* t, const void* pool, uint64_t pool_rows)
   StreamArgs ra;
   ra.pool = static_cast<const unsigned char*>(pool);
   ra.rowmap = image_of(t).rowmap;
+  ra.trig = image_of(t).trig;
   ra.pool_last = pool_last_of(pool_rows);
   return ra;
 }

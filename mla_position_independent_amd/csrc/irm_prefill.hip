@@ -133,6 +133,7 @@ irm_status launch_prefill(const irm_table* t, const void* q_lat, const void* q_r
                           void* out, float* lse, hipStream_t s) {
   PrefillArgs a = prefill_args(q_lat, q_rope, q_pos0, n_q, pool, pool_rows, n_heads, scale, out, lse);
   a.ra.rowmap = image_of(t).rowmap;
+  a.ra.trig = image_of(t).trig;
   a.seq_base = image_of(t).seq_base;
   for (int i = 0; i < (int)kPairs; ++i) a.f.w[i] = t->inv_freq[i];
   return launch<false>(a, s, "irm_mla_prefill_tail");
