@@ -360,10 +360,15 @@ def test_decode_split_invariance_and_determinism():
     assert np.array_equal(again[0], res[4][0]) and np.array_equal(again[1], res[4][1])
 
 
-def test_decode_fused_equals_gather_then_decode():
+@pytest.mark.parametrize("heads,tiny", [(32, False), (128, False), (128, True)])
+def test_decode_fused_equals_gather_then_decode(heads, tiny):
     """Rotating on load equals assembling first and decoding the assembled
-    buffer as fresh rows (both round the rotated k_r to bf16 once)."""
-    w = random_table(12, [1500, 900, 64], heads=32)
+    buffer as fresh rows (both round the rotated k_r to bf16 once, with the
+    same per-entry cos/sin): the 16-head-group kernel, the 64-head-block
+    kernel, and the latter on 1..7-row chunks, whose slices hold more deltas
+    than the per-wave table."""
+    kw = {"len_fn": _tiny_chunks, "p_hit": 0.9} if tiny else {}
+    w = random_table(12, [1500, 900, 64], heads=heads, **kw)
     pool = irm.to_device_bf16(w.pool)
     t = _table(w)
     fused = _gpu_decode(w, 4, table=t, pool=pool)
