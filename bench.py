@@ -149,6 +149,30 @@ def time_leg(fn, steps: int, warmup: int, inner_events: bool = True):
     return (t1 - t0) * 1e3 / steps, (sum(kern) / len(kern)) if kern else None
 
 
+_SCRUB = []
+
+
+def time_cold(fn, n: int = 5):
+    """Median event time (ms) of fn over n launches, each after a 512 MB
+    write that evicts the 256 MB Infinity Cache (the scrub is outside the
+    events): what the kernel does when none of its inputs sit in a cache."""
+    import torch
+    if not _SCRUB:
+        _SCRUB.append(torch.empty(512 << 20, dtype=torch.uint8, device="cuda"))
+    scrub = _SCRUB[0]
+    ts = []
+    for k in range(n):
+        scrub.fill_(k & 0xff)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
 def leg_gather(args, irm, torch, synth):
     log("rotate-gather: generating 64 x 32768-token batch")
     w = synth.rotate_gather_batch()
@@ -170,13 +194,17 @@ def leg_gather(args, irm, torch, synth):
     alg_bytes = 2 * ROW_BYTES * tokens
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic("rotate_gather_kernel")
-    log(f"rotate-gather: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms, {achieved:.0f} GB/s")
+    cold_ms = time_cold(lambda: irm.rotate_gather(t, pool, out=out))
+    log(f"rotate-gather: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms, {achieved:.0f} GB/s; "
+        f"after a cache scrub {cold_ms:.3f} ms")
     res = {
         "tokens": tokens, "ms_per_step": ms, "kernel_ms": kern_ms,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "rotate_gather_kernel",
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "cold_cache_kernel_ms": round(cold_ms, 4),
+                     "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "workload": w, "table": t,
     }
     return res
@@ -200,6 +228,7 @@ def leg_decode(args, irm, torch, synth, name, make):
             ev[1].record()
 
     ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    cold_ms = time_cold(lambda: step(None))
     # the split pass runs one 16-head group per workgroup unless the head
     # count is a multiple of 64 (four groups share every KV tile)
     kernel = "decode_shared_kernel" if H % 64 == 0 else "decode_private_kernel"
@@ -208,14 +237,17 @@ def leg_decode(args, irm, torch, synth, name, make):
     alg_bytes = kv + qo
     flops = 2 * (576 + 512) * H * t.total_rows
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"{name}: {kern_ms:.3f} ms/call, {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s")
+    log(f"{name}: {kern_ms:.3f} ms/call, {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s; "
+        f"after a cache scrub {cold_ms:.3f} ms")
     return {
         "workload": w.name, "ms_per_call": round(kern_ms, 4), "tokens": t.total_rows, "n_splits": w.n_splits,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(kernel + ":" + w.name),
                      "kernel": kernel + " + decode_combine_kernel",
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "cold_cache_kernel_ms": round(cold_ms, 4),
+                     "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
     }
 
