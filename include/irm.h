@@ -200,7 +200,11 @@ irm_status irm_mla_decode_workspace(const irm_table* t, uint32_t n_heads, uint32
  *   n_splits: KV splits per sequence (0 = default); every sequence must hold
  *   at least one row (EINVAL).
  *   device workspace of at least irm_mla_decode_workspace bytes (EWORKSPACE).
- * Each query attends to every row of its sequence.
+ * Each query attends to every row of its sequence.  Reused rows are turned
+ * with the table's per-entry cos/sin (the values irm_rotate_gather applies,
+ * from the last irm_table_upload / irm_table_set_rope on the stream) and
+ * rounded to bf16 before the score product, so decoding the rotate-gather
+ * output as fresh rows gives the same bits.
  */
 irm_status irm_mla_decode(const void* q_latent, const void* q_rope, const irm_table* t,
                           const void* pool, uint64_t pool_rows, uint32_t n_heads,
@@ -211,7 +215,8 @@ irm_status irm_mla_decode(const void* q_latent, const void* q_rope, const irm_ta
  * Chunked tail-prefill for one sequence (the table must hold exactly one
  * sequence of N rows): n_q query tokens at positions q_pos0 .. q_pos0+n_q-1
  * attend causally (row t visible to query i iff t <= q_pos0 + i) over the
- * assembled cache, with k_r rotated on load.
+ * assembled cache, with k_r rotated on load (with the table's per-entry
+ * cos/sin, as in irm_mla_decode).
  *   device q_latent bf16 [n_q][n_heads][512]; q_rope bf16 [n_q][n_heads][64];
  *   device out bf16 [n_q][n_heads][512]; lse optional float [n_q][n_heads].
  *   0 <= q_pos0, 1 <= n_q, q_pos0 + n_q <= N (ERANGE); n_heads a multiple of
