@@ -239,8 +239,13 @@ def leg_decode(args, irm, torch, synth, name, make):
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     log(f"{name}: {kern_ms:.3f} ms/call, {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s; "
         f"after a cache scrub {cold_ms:.3f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"{name}: oracle on a sample of the batch")
+        cpu = cpu_baseline_decode(w, args.cpu_seconds_legs)
     return {
         "workload": w.name, "ms_per_call": round(kern_ms, 4), "tokens": t.total_rows, "n_splits": w.n_splits,
+        "cpu_baseline": cpu,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(kernel + ":" + w.name),
@@ -250,6 +255,42 @@ def leg_decode(args, irm, torch, synth, name, make):
                      "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
     }
+
+
+def leg_tiny(args, irm, torch, synth):
+    """The 1-sequence, 1024-row, 16-head decode: a latency case, reported in
+    microseconds per call (split pass + combine), with the oracle beside it."""
+    w = synth.tiny_decode()
+    pool = irm.to_device_bf16(w.pool)
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(irm.rope_inv_freq(w.theta))
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    out = torch.empty((1, w.n_heads, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(irm.decode_workspace_bytes(t, w.n_heads, 4), dtype=torch.uint8, device="cuda")
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        irm.mla_decode(ql, qr, t, pool, n_splits=4, scale=w.scale, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            reps = 0
+            while reps == 0 or time.perf_counter() - t0 < 1.0:
+                c, k = _oracle_rows(w, 0, oracle.rope_inv_freq(w.theta))
+                oracle.mla_decode(oracle.bf16_to_f64(w.q_lat[0]), oracle.bf16_to_f64(w.q_rope[0]), c, k, w.scale)
+                reps += 1
+            cpu = {"value": round((time.perf_counter() - t0) / reps * 1e6, 1), "unit": "us per call", "cores": 1,
+                   "kind": "oracle", "host": host_cpu(), "sample": f"the whole case, {reps} calls"}
+    log(f"tiny decode: {kern_ms * 1e3:.1f} us per call")
+    return {"workload": w.name, "us_per_call": round(kern_ms * 1e3, 2), "n_splits": 4,
+            "kernel": "decode_private_kernel + decode_combine_kernel", "cpu_baseline": cpu}
 
 
 def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = True):
@@ -295,8 +336,13 @@ def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = T
     log(f"tail-prefill: {ms:.3f} ms/call (rotate-gather + prefill over the assembled cache; prefill kernel "
         f"{kern_ms:.3f} ms, {achieved:.0f} TFLOP/s); rotation on load in one kernel: "
         + ("not timed" if fused_ms is None else f"{fused_ms:.3f} ms"))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("tail-prefill: oracle on the first queries")
+        cpu = cpu_baseline_prefill(w, args.cpu_seconds_legs)
     return {
         "workload": w.name, "ms_per_call": round(ms, 4), "queries": nq, "kv_rows": t.total_rows,
+        "cpu_baseline": cpu,
         "call": "irm_rotate_gather + irm_mla_prefill_assembled",
         "prefill_kernel_ms": round(kern_ms, 4),
         "fused_rotate_on_load_ms": None if fused_ms is None else round(fused_ms, 4),
@@ -478,9 +524,84 @@ def cpu_baseline(w, seconds: float):
             done_tokens += g.shape[0]
             done_req += 1
     return {"value": round(done_tokens / spent, 1), "unit": "assembled KV tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"first {done_req} of {w.n_seq} requests ({done_tokens} tokens), "
                       f"{spent:.1f} s single-threaded float64 numpy"}
+
+
+def host_cpu() -> str:
+    """Host cores and CPU model, for the oracle baselines."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"1 of {os.cpu_count()} host cores ({model})"
+
+
+def _oracle_rows(w, b, inv):
+    """Assembled rows of sequence b by the oracle (table expansion, float64
+    rotation)."""
+    import numpy as np
+    import oracle
+    lo, hi = int(w.seq_first[b]), int(w.seq_first[b + 1])
+    (g, d, _), = oracle.expand_table(w.chunks[lo:hi], np.array([0, hi - lo]), w.pool.shape[0])
+    return oracle.assemble_rows(w.pool, g, d, inv)
+
+
+def cpu_baseline_decode(w, seconds: float):
+    """The oracle, single-threaded, on whole sequences of a decode batch (row
+    assembly and attention) until ``seconds`` have been spent (at least one);
+    algorithmic bytes per second as for the GPU leg."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    inv = oracle.rope_inv_freq(w.theta)
+    done, tokens, spent = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while done < w.n_seq and (spent < seconds or done == 0):
+            t0 = time.perf_counter()
+            c, k = _oracle_rows(w, done, inv)
+            oracle.mla_decode(oracle.bf16_to_f64(w.q_lat[done]), oracle.bf16_to_f64(w.q_rope[done]), c, k, w.scale)
+            spent += time.perf_counter() - t0
+            tokens += c.shape[0]
+            done += 1
+    nbytes = ROW_BYTES * tokens + done * w.n_heads * (576 + 512) * 2
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
+            "sample": f"first {done} of {w.n_seq} sequences ({tokens} cached tokens, {w.n_heads} heads), "
+                      f"{spent:.1f} s single-threaded float64 numpy"}
+
+
+def cpu_baseline_prefill(w, seconds: float):
+    """The oracle, single-threaded: the 65536-row cache assembled once (timed
+    apart), then the first queries of the tail in blocks of 4 until
+    ``seconds`` of attention have been spent; algorithmic flops per second of
+    the attention as for the GPU leg."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+
+    inv = oracle.rope_inv_freq(w.theta)
+    nq, H = w.q_lat.shape[0], w.n_heads
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        c, k = _oracle_rows(w, 0, inv)
+        assemble_s = time.perf_counter() - t0
+        done, spent, flops = 0, 0.0, 0.0
+        while done < nq and (spent < seconds or done == 0):
+            hi = min(nq, done + 4)
+            t0 = time.perf_counter()
+            oracle.mla_prefill_tail(oracle.bf16_to_f64(w.q_lat[done:hi]), oracle.bf16_to_f64(w.q_rope[done:hi]),
+                                    c, k, w.q_pos0 + done, w.scale)
+            spent += time.perf_counter() - t0
+            flops += sum(w.q_pos0 + i + 1 for i in range(done, hi)) * H * 2 * (576 + 512)
+            done = hi
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
+            "sample": f"first {done} of {nq} queries over {c.shape[0]} rows ({spent:.1f} s of attention; the "
+                      f"cache assembly took {assemble_s:.1f} s apart), single-threaded float64 numpy"}
 
 
 def main():
@@ -488,9 +609,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="gather,decode,long_decode,prefill,nonabsorbed,gqa,producer",
+    ap.add_argument("--legs", default="gather,tiny,decode,long_decode,prefill,nonabsorbed,gqa,producer",
                     help="comma list; without gather only the named legs run (profiling, no JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds-legs", type=float, default=5.0,
+                    help="oracle seconds per decode / prefill leg (its own cpu_baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling HBM counters) and exit")
@@ -530,11 +653,14 @@ def main():
 
     legs = [x.strip() for x in args.legs.split(",") if x.strip()]
     if args.profile or "gather" not in legs:
-        # profiling mode: run the requested legs only, no JSON line
+        # profiling mode: run the requested legs only, no JSON line, no oracle
+        args.no_cpu_baseline = True
         g = None
         for name in legs:
             if name == "gather":
                 g = leg_gather(args, irm, torch, synth)
+            elif name == "tiny":
+                leg_tiny(args, irm, torch, synth)
             elif name == "decode":
                 leg_decode(args, irm, torch, synth, "batched decode", synth.batched_decode)
             elif name == "long_decode":
@@ -552,6 +678,8 @@ def main():
         return
     g = leg_gather(args, irm, torch, synth)
     extra = {}
+    if "tiny" in legs:
+        extra["tiny_decode"] = leg_tiny(args, irm, torch, synth)
     if "decode" in legs:
         extra["decode"] = leg_decode(args, irm, torch, synth, "batched decode", synth.batched_decode)
     if "long_decode" in legs:
