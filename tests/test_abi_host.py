@@ -165,3 +165,73 @@ def test_nonabsorbed_validation_errors():
     assert pf(q_pos0=-1) == "ERANGE" and pf(n_q=0) == "ERANGE" and pf(q_pos0=60, n_q=5) == "ERANGE"
     assert pf(kvh=None) == "EINVAL" and pf(kv=A + 2) == "EINVAL" and pf(q=A + 8) == "EINVAL"
 
+
+
+# ---------------------------------------------------------------- property-based
+from hypothesis import HealthCheck, given, settings, strategies as st
+
+_POOL = 5000
+
+
+@st.composite
+def _tables(draw):
+    """Chunk tables that are valid by construction (contiguous p_tgt from 0,
+    fresh rows below 32 and fresh entries with p_src == p_tgt) with, now and
+    then, one planted defect: a pool row past the end, an unknown flag bit, a
+    gap or overlap in p_tgt, a hit below position 32, a fresh entry with
+    p_src != p_tgt, a zero length, or an extreme delta."""
+    n_seq = draw(st.integers(1, 4))
+    rows, seq_first = [], [0]
+    for _ in range(n_seq):
+        pos = 0
+        for _ in range(draw(st.integers(0, 6))):
+            ln = draw(st.integers(1, 120))
+            fresh = pos < 32 or draw(st.booleans())
+            if pos < 32 and pos + ln > 32 and draw(st.booleans()):
+                ln = 32 - pos                    # fresh entry ending exactly at the carve-out
+            p_src = pos if fresh else draw(st.integers(-(2 ** 20), 2 ** 20))
+            pool_row = draw(st.integers(0, _POOL - ln))
+            rows.append([pool_row, ln, p_src, pos, FRESH if fresh else 0])
+            pos += ln
+        seq_first.append(len(rows))
+    if rows and draw(st.integers(0, 3)) == 0:     # plant one defect
+        i = draw(st.integers(0, len(rows) - 1))
+        kind = draw(st.integers(0, 6))
+        r = rows[i]
+        if kind == 0:
+            r[0] = _POOL - r[1] + draw(st.integers(1, 50))
+        elif kind == 1:
+            r[4] |= 1 << draw(st.integers(1, 31))
+        elif kind == 2:
+            r[3] += draw(st.sampled_from([-1, 1, 7]))
+        elif kind == 3:
+            r[4] = 0
+            r[2] = r[3] + 5
+        elif kind == 4:
+            r[4] = FRESH
+            r[2] = r[3] + draw(st.integers(1, 9))
+        elif kind == 5:
+            r[1] = 0
+        else:
+            r[2] = r[3] - draw(st.sampled_from([2 ** 31 - 1, -(2 ** 31) + r[3] + 1]))
+            r[4] = 0
+    return rows, seq_first
+
+
+@settings(max_examples=400, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(_tables())
+def test_table_builder_agrees_with_oracle_on_generated_tables(case):
+    rows, seq_first = case
+    c = np.array([tuple(int(x) for x in r) for r in rows], dtype=CHUNK_DTYPE) if rows else np.zeros(0, CHUNK_DTYPE)
+    sf = np.array(seq_first, dtype=np.uint32)
+    try:
+        oracle.expand_table(c, sf, _POOL)
+        ocode = "OK"
+    except oracle.TableError as e:
+        ocode = e.code
+    if ocode == "OK":
+        _compare_with_oracle(c, sf, _POOL)
+    else:
+        with pytest.raises(irm.IrmError) as e:
+            irm.Table(c, sf, _POOL)
+        assert e.value.code == ocode
