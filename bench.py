@@ -629,7 +629,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by request "
-              "or sequence with no exchange, and this build measures the one-GPU share.", file=sys.stderr)
+              "or sequence with no exchange, and the benchmark measures one GPU's share.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -14,7 +14,7 @@ token, an O(N d_K) correction per KV head, while MLA corrects only the
 they are.  The same delta rotation applies: R(p_tgt - p_src) R(p_src) =
 R(p_tgt).
 
-Readings where the pages are silent (also in the design doc): a row is
+Readings where the pages are silent: a row is
 [K of n_kv_heads heads | V of n_kv_heads heads], each head head_dim wide, bf16;
 the rotation covers the whole head_dim with the half-split pairing of
 GQA models (element i turns with element i + head_dim/2, frequency

@@ -11,7 +11,7 @@ key at run time): the key of row t for head h is [W_UK[h] c_KV[t], k_r[t]],
 the value is derived from c_KV alone, and only k_r carries the position, so
 the rotated k_r of the assembled cache is used as it is.
 
-Readings where the pages are silent (also in the design doc): W_UK[h] and W_UV[h]
+Readings where the pages are silent: W_UK[h] and W_UV[h]
 are [128][512] per head (output feature, latent input), the nope part of the
 key and the value are both 128 wide, the query is [q_nope 128 | q_rope 64]
 per head, the score scale is 1/sqrt(192), and the causal mask is the one of

@@ -18,8 +18,7 @@ it follows:
   (worked example of delta).
 
 Readings of points the pages leave open (RoPE pair layout, theta, scale,
-masks, carve-out extent, fresh rows) are listed in the design doc; the ones used
-here are: interleaved RoPE pairs (2i, 2i+1) with omega_i = theta^(-2i/64),
+masks, carve-out extent, fresh rows), as used here: interleaved RoPE pairs (2i, 2i+1) with omega_i = theta^(-2i/64),
 softmax scale 1/sqrt(192), decode attends to every cached row, tail-prefill
 query i attends to rows t <= q_pos0 + i, rows at positions < 32 must come
 from fresh entries, and fresh entries have p_src == p_tgt.

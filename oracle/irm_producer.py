@@ -20,7 +20,7 @@ Plain, slow, single-threaded Python integers.  What the pages fix and where:
   xxHash64.  gist.science summary, section 2.2: the Gear hash rolls over
   64-token windows.
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
 
 * Gear state: 64-bit, h <- (h << 1) + gear(token) mod 2^64, so a token's
   contribution leaves the state after 64 steps (the 64-token window).  The

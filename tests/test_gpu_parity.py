@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Bars (derived in the design doc):
+Bars:
 * gather indices and deltas, c_KV bytes, and fresh / delta-0 k_r bytes: bit-exact;
 * rotated k_r (float side output): relative L2 <= 1e-5; bf16 k_r within one
   bf16 ulp of the oracle's exact value;
