@@ -198,7 +198,12 @@ irm_status irm_mla_decode_workspace(const irm_table* t, uint32_t n_heads, uint32
  *   [n_seq][n_heads] (natural-log sum of exp of the scaled scores);
  *   n_heads a multiple of 16, <= 128 (else EUNSUPPORTED); scale > 0 finite;
  *   n_splits: KV splits per sequence (0 = default); every sequence must hold
- *   at least one row (EINVAL).
+ *   at least one row (EINVAL).  At 64 or more heads (a multiple of 64), when
+ *   the batch has more (sequence, split, 64-head block) triples than the
+ *   device has compute units, one workgroup streams several consecutive
+ *   splits as one softmax run, so the rounding order (not the result within
+ *   float accuracy) depends on the device's compute-unit count; a given
+ *   device, table and split count always give the same bits.
  *   device workspace of at least irm_mla_decode_workspace bytes (EWORKSPACE).
  * Each query attends to every row of its sequence.  Reused rows are turned
  * with the table's per-entry cos/sin (the values irm_rotate_gather applies,

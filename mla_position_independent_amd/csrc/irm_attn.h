@@ -587,14 +587,6 @@ __device__ __forceinline__ void slice_rot_store(unsigned char* kr, uint32_t row0
 // Flat mode (kFlat): the rows are an assembled cache, row g of the stream is
 // row g of the buffer and every delta is 0, so no row maps are copied and
 // nothing is rotated.
-//
-// Segments: with seg_tiles > 0 the rows form consecutive segments of
-// seg_tiles tiles (the last one may be shorter), each with its own softmax
-// state.  The scorers hand (m, l) of a segment to seg_end(k, m, l) after its
-// last tile's softmax and restart from -inf; the accumulators hand O to
-// seg_end(k, o) after that tile's PV and restart from zero.  The first tile
-// of a segment always moves the reference maximum away from -inf, and its
-// rescale factor (0) then meets the zeroed O.
 // ---------------------------------------------------------------------------
 constexpr int kRoleThreads = 2 * kThreads;
 // c_KV rows of each slice that the scorer copies: all of them, since the
@@ -613,10 +605,9 @@ __device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirs
 // accumulator of that slice copies the rest, its k_r and row maps), from the
 // row-map records the accumulator published one barrier earlier, and waits
 // for them before the barrier that ends iteration t+1.
-template <bool kFlat, class Last, class SegEnd>
+template <bool kFlat, class Last>
 __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
-                                             float c, Last&& last, const bf16x8_t (&qb)[18], float& m, float& l,
-                                             uint32_t seg_tiles, SegEnd&& seg_end) {
+                                             float c, Last&& last, const bf16x8_t (&qb)[18], float& m, float& l) {
   const uint32_t lane = threadIdx.x & 63, s = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
@@ -679,11 +670,6 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
     sm.pfrag[t & 1][s][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
     if (hq == 0) sm.alpha[t & 1][s][hr] = alpha;
     if (lane == 0) sm.scaled[t & 1][s] = moved ? 1u : 0u;
-    if (seg_tiles && ((t + 1) % seg_tiles == 0 || t + 1 == nt)) {  // last tile of a segment
-      seg_end(t / seg_tiles, m, l);
-      m = -INFINITY;
-      l = 0.f;
-    }
     wait_dma_but<kScoreRows>();  // this wave's rows of tile t+1 have landed
     __syncthreads();
   }
@@ -697,10 +683,9 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
 // iteration ahead, so that the only LDS round trip on the way from one
 // barrier to the next is the one for the P / C^T fragments and the k_r to
 // rotate.
-template <bool kFlat, class SegEnd>
+template <bool kFlat>
 __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm, uint32_t g_begin, uint32_t n,
-                                             f32x4_t (&o)[kSplitGroups][kSplitNb], uint32_t seg_tiles,
-                                             SegEnd&& seg_end) {
+                                             f32x4_t (&o)[kSplitGroups][kSplitNb]) {
   const uint32_t lane = threadIdx.x & 63, j = wave_id() - kSplitGroups, hr = lane & 15;
   const uint32_t nt = (n + kTileRows - 1) / kTileRows;
   if (nt == 0) return;
@@ -814,15 +799,6 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
       mid();
     }
     if constexpr (!kFlat) slice_issue_rowmap<kTileSlice>(ra, g0(t + 4), ws.rm[(t + 4) % kTileRm]);
-    if constexpr (B) {
-      if (seg_tiles && (t % seg_tiles == 0 || t == nt)) {  // tile t-1 closed a segment
-        seg_end((t - 1) / seg_tiles, o);
-#pragma unroll
-        for (int g = 0; g < kSplitGroups; ++g)
-#pragma unroll
-          for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    }
     __syncthreads();
   };
 

@@ -22,10 +22,11 @@ struct DecodeArgs {
   const uint32_t* seq_base;
   const uint4* q_lat;
   const uint4* q_rope;
-  float* ws_acc;  // [n_seq][n_splits][n_heads][512], unnormalised
-  float* ws_ml;   // [n_seq][n_splits][n_heads][2]: base-2 max, sum
+  float* ws_acc;  // [n_seq][n_parts][n_heads][512], unnormalised
+  float* ws_ml;   // [n_seq][n_parts][n_heads][2]: base-2 max, sum
   uint32_t n_seq, n_heads, n_groups, n_splits;
-  uint32_t splits_per_wg;  // shared-tile kernel: consecutive splits per workgroup (divides n_splits)
+  uint32_t splits_per_wg;  // shared-tile kernel: consecutive splits per workgroup (divides n_splits);
+                           // n_parts = n_splits / splits_per_wg partial states per sequence
   float scale_log2;
   InvFreq f;
 };
@@ -194,13 +195,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
 // waves.  Scoring wave s holds head group 4 blk + s; accumulating wave j sums
 // columns 128 j .. 128 j + 127 of all four groups (score_stream /
 // value_stream), so the KV is copied once per 64 heads instead of once per
-// 16.  The U splits are contiguous rows, streamed as one run of tiles with a
-// segment per split (splits are whole multiples of 64 rows, so segments
-// start on tile boundaries), which keeps the copy pipeline full across split
-// boundaries and pays the workgroup's start-up once per run.  Each segment's
-// partial state goes straight to the workspace: O from the accumulating
-// waves, (m, l) from the scoring waves; splits of the run that hold no rows
-// get the empty state (O = 0, m = -inf, l = 0).
+// 16.  The U splits are contiguous rows, streamed as one softmax run, which
+// keeps the copy pipeline full and pays the workgroup's start-up once; the
+// run's partial state goes to the workspace as one part (O from the
+// accumulating waves, (m, l) from the scoring waves), so the combine pass
+// reads n_splits / U parts per sequence.  A run without rows leaves the
+// empty state (O = 0, m = -inf, l = 0).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) SplitSmem sm;
@@ -211,38 +211,31 @@ __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeAr
   const uint32_t hb = slot % n_blk;
   const uint32_t br = (slot / n_blk) * 8 + xcd;
   if (br >= a.n_seq * n_runs) return;
-  const uint32_t b = br / n_runs, sp0 = (br % n_runs) * U;
+  const uint32_t b = br / n_runs, run = br % n_runs;
 
   const uint32_t base = a.seq_base[b], N = a.seq_base[b + 1] - base;
   const uint32_t per = split_len(N, a.n_splits);
-  const uint32_t r0 = min(N, sp0 * per), r1 = min(N, r0 + U * per);
-  const uint32_t seg_tiles = per / kTileRows > 0 ? per / kTileRows : 1;
-  const uint32_t nt = (r1 - r0 + kTileRows - 1) / kTileRows;
-  const uint32_t n_seg = (nt + seg_tiles - 1) / seg_tiles;  // splits of the run that hold rows
+  const uint32_t r0 = min(N, run * U * per), r1 = min(N, r0 + U * per);
 
   const uint32_t lane = threadIdx.x & 63, w = wave_id(), hq = lane >> 4, hr = lane & 15;
   const uint32_t g0 = hb * kSplitGroups;  // first head group of the block
-  auto pbase = [&](uint32_t k) { return ((size_t)b * a.n_splits + sp0 + k) * a.n_heads + g0 * 16; };
+  const size_t pbase = (size_t)br * a.n_heads + g0 * 16;  // part (b, run) of the first head
   fill_omega(sm.s.omega, a.f);
 
   if (w < kSplitGroups) {  // scoring wave: head group g0 + w
     bf16x8_t qb[18];
     load_q<false>(a.q_lat, a.q_rope, b, a.n_heads, (g0 + w) * 16 + hr, qb);
     float m = -INFINITY, l = 0.f;
-    auto put_ml = [&](uint32_t k, float mk, float lk) {
-      lk += __shfl_xor(lk, 16);
-      lk += __shfl_xor(lk, 32);
-      if (hq == 0) {
-        float* d = a.ws_ml + (pbase(k) + 16 * w + hr) * 2;
-        d[0] = mk;
-        d[1] = (mk == -INFINITY) ? 0.f : lk;
-      }
-    };
     __syncthreads();
     score_stream<false>(a.ra, sm, base + r0, r1 - r0, a.scale_log2,
-                 [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l, seg_tiles,
-                 put_ml);
-    for (uint32_t k = n_seg; k < U; ++k) put_ml(k, -INFINITY, 0.f);
+                        [&](uint32_t, uint32_t nrows) -> int32_t { return (int32_t)nrows - 1; }, qb, m, l);
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (hq == 0) {
+      float* d = a.ws_ml + (pbase + 16 * w + hr) * 2;
+      d[0] = m;
+      d[1] = (m == -INFINITY) ? 0.f : l;
+    }
     return;
   }
 
@@ -253,37 +246,36 @@ __global__ __launch_bounds__(kRoleThreads, 1) void decode_shared_kernel(DecodeAr
   for (int g = 0; g < kSplitGroups; ++g)
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto put_o = [&](uint32_t k, const f32x4_t(&ok)[kSplitGroups][kSplitNb]) {
-#pragma unroll
-    for (int g = 0; g < kSplitGroups; ++g) {
-      float* dst = a.ws_acc + (pbase(k) + 16 * g + hr) * IRM_D_LATENT + kSplitCols * j + 4 * hq;
-#pragma unroll
-      for (int nb = 0; nb < kSplitNb; ++nb)
-        *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(ok[g][nb][0], ok[g][nb][1], ok[g][nb][2], ok[g][nb][3]);
-    }
-  };
   __syncthreads();
-  value_stream<false>(a.ra, sm, base + r0, r1 - r0, o, seg_tiles, put_o);
-  for (uint32_t k = n_seg; k < U; ++k) put_o(k, o);  // o is zero here
+  value_stream<false>(a.ra, sm, base + r0, r1 - r0, o);
+#pragma unroll
+  for (int g = 0; g < kSplitGroups; ++g) {
+    float* dst = a.ws_acc + (pbase + 16 * g + hr) * IRM_D_LATENT + kSplitCols * j + 4 * hq;
+#pragma unroll
+    for (int nb = 0; nb < kSplitNb; ++nb)
+      *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[g][nb][0], o[g][nb][1], o[g][nb][2], o[g][nb][3]);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // split-KV decode, pass 2
 // ---------------------------------------------------------------------------
 // One workgroup per (sequence, head), one float4 of the 512 columns per
-// thread.  kMax > 0: at most kMax splits, every load issued before any
-// arithmetic; kMax = 0: any count, in batches.  Every split slot holds finite
-// partials (zeros for a split without rows, whose maximum is -inf and whose
-// weight is 0), so no load depends on another split's values.
+// thread, over the n_parts partial states of the sequence (one per split, or
+// one per run of splits of the 64-head kernel).  kMax > 0: at most kMax
+// parts, every load issued before any arithmetic; kMax = 0: any count, in
+// batches.  Every part holds finite values (zeros for a part without rows,
+// whose maximum is -inf and whose weight is 0), so no load depends on
+// another part's values.
 template <int kMax>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws_acc,
                                                              const float* __restrict__ ws_ml,
                                                              uint16_t* __restrict__ out,
                                                              float* __restrict__ lse,
-                                                             uint32_t n_heads, uint32_t n_splits) {
+                                                             uint32_t n_heads, uint32_t n_parts) {
   const uint32_t bh = blockIdx.x;
   const uint32_t b = bh / n_heads, h = bh % n_heads;
-  const size_t p0 = (size_t)b * n_splits * n_heads + h;  // partial of split s: p0 + s * n_heads
+  const size_t p0 = (size_t)b * n_parts * n_heads + h;  // part s: p0 + s * n_heads
   const float2* ml = reinterpret_cast<const float2*>(ws_ml);
   auto acc_of = [&](uint32_t s) {
     return reinterpret_cast<const float4*>(ws_acc + (p0 + (size_t)s * n_heads) * IRM_D_LATENT)[threadIdx.x];
@@ -303,8 +295,8 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
     float4 v[kMax];
 #pragma unroll
     for (int s = 0; s < kMax; ++s) {
-      m2[s] = (uint32_t)s < n_splits ? ml[p0 + (size_t)s * n_heads] : make_float2(-INFINITY, 0.f);
-      v[s] = (uint32_t)s < n_splits ? acc_of(s) : make_float4(0.f, 0.f, 0.f, 0.f);
+      m2[s] = (uint32_t)s < n_parts ? ml[p0 + (size_t)s * n_heads] : make_float2(-INFINITY, 0.f);
+      v[s] = (uint32_t)s < n_parts ? acc_of(s) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int s = 0; s < kMax; ++s) mx = fmaxf(mx, m2[s].x);
@@ -312,9 +304,9 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
     for (int s = 0; s < kMax; ++s) add(m2[s], v[s]);
   } else {
 #pragma unroll 8
-    for (uint32_t s = 0; s < n_splits; ++s) mx = fmaxf(mx, ml[p0 + (size_t)s * n_heads].x);
+    for (uint32_t s = 0; s < n_parts; ++s) mx = fmaxf(mx, ml[p0 + (size_t)s * n_heads].x);
 #pragma unroll 8
-    for (uint32_t s = 0; s < n_splits; ++s) add(ml[p0 + (size_t)s * n_heads], acc_of(s));
+    for (uint32_t s = 0; s < n_parts; ++s) add(ml[p0 + (size_t)s * n_heads], acc_of(s));
   }
   const float inv = 1.f / L;
   uint2 w;
@@ -400,14 +392,15 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
     hipLaunchKernelGGL(decode_private_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   irm_status st = launch_check("irm_mla_decode: split kernel");
   if (st != IRM_OK) return st;
+  const uint32_t n_parts = n_splits / a.splits_per_wg;
   const dim3 cgrid(t->n_seq * n_heads), cblock(128);
   uint16_t* o16 = static_cast<uint16_t*>(out);
-  if (n_splits <= 4)
-    hipLaunchKernelGGL(decode_combine_kernel<4>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_splits);
-  else if (n_splits <= 16)
-    hipLaunchKernelGGL(decode_combine_kernel<16>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_splits);
+  if (n_parts <= 4)
+    hipLaunchKernelGGL(decode_combine_kernel<4>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_parts);
+  else if (n_parts <= 16)
+    hipLaunchKernelGGL(decode_combine_kernel<16>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_parts);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<0>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_splits);
+    hipLaunchKernelGGL(decode_combine_kernel<0>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_parts);
   return launch_check("irm_mla_decode: combine kernel");
 }
 

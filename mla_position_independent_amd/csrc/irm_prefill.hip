@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
                    const int64_t last = lim - (int64_t)t * kTileRows;
                    return last > kTileRows ? kTileRows : (last < -1 ? -1 : (int32_t)last);
                  },
-                 qb, m, l, 0, [](uint32_t, float, float) {});
+                 qb, m, l);
     split_publish(sm, m, l);
     if (a.lse && qi < a.n_q && hq == 0)
       a.lse[(size_t)qi * a.n_heads + head] = (sm.ml[w][hr][0] + log2f(sm.ml[w][hr][1])) * kLn2;
@@ -78,8 +78,7 @@ __global__ __launch_bounds__(kRoleThreads, 1) void prefill_kernel(PrefillArgs a)
 #pragma unroll
     for (int nb = 0; nb < kSplitNb; ++nb) o[g][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  value_stream<kFlat>(a.ra, sm, kFlat ? 0u : a.seq_base[0], rows, o, 0,
-                      [](uint32_t, const f32x4_t(&)[kSplitGroups][kSplitNb]) {});
+  value_stream<kFlat>(a.ra, sm, kFlat ? 0u : a.seq_base[0], rows, o);
   split_publish_wait();
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g) {

@@ -336,8 +336,8 @@ def test_decode_rescale_paths(heads):
 @pytest.mark.parametrize("heads,n_seq", [(64, 40), (128, 20)])
 def test_decode_split_runs(heads, n_seq):
     """Enough (sequence, split) pairs that one workgroup of the 64-head kernel
-    streams several consecutive splits (two on a 256-CU part) as segments of
-    one run; ragged lengths leave partial and empty splits inside the runs."""
+    streams several consecutive splits (two on a 256-CU part) as one run with
+    one partial state; ragged lengths leave partial and empty runs."""
     rng = np.random.default_rng(34)
     lens = [int(x) for x in rng.integers(1, 1200, size=n_seq - 1)] + [2048]
     w = random_table(34, lens, heads=heads, p_hit=0.8)
