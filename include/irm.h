@@ -95,6 +95,18 @@ const char* irm_last_error(void);
 irm_status irm_rope_inv_freq(double theta, double* inv_freq);
 
 /*
+ * Standard RoPE inverse frequencies for a rotary slice of any even width:
+ * inv_freq[i] = theta^(-2i/dim), i = 0 .. dim/2 - 1, in double precision
+ * (for example the whole head_dim of a GQA/MHA key, which the comparison
+ * path irm_gqa_rotate_gather turns; the pages insist that the rotation use
+ * the model's own rotary frequencies: gentlecold.top article, section 11).
+ * irm_rope_inv_freq(theta, f) equals irm_rope_inv_freq_dim(theta, 64, f).
+ *   host out inv_freq[dim / 2].  EINVAL if theta <= 1 or not finite, dim odd,
+ *   below 2 or above 4096, or inv_freq is NULL.
+ */
+irm_status irm_rope_inv_freq_dim(double theta, uint32_t dim, double* inv_freq);
+
+/*
  * Validate a chunk table and build its device image in library-owned host
  * memory.  Makes no HIP call (usable without a GPU).
  *   host chunks[n_chunks]; host seq_first[n_seq + 1]: sequence s owns

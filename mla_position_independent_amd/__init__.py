@@ -32,7 +32,7 @@ CHUNK_DTYPE = np.dtype(
 )
 
 EXPORTS = (
-    "irm_last_error", "irm_rope_inv_freq", "irm_table_create", "irm_table_destroy",
+    "irm_last_error", "irm_rope_inv_freq", "irm_rope_inv_freq_dim", "irm_table_create", "irm_table_destroy",
     "irm_table_info", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
     "irm_table_set_rope",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "irm_last_error": (ctypes.c_char_p, []),
         "irm_rope_inv_freq": (ctypes.c_int, [ctypes.c_double, vp]),
+        "irm_rope_inv_freq_dim": (ctypes.c_int, [ctypes.c_double, u32, vp]),
         "irm_table_create": (ctypes.c_int, [vp, u32, vp, u32, u64, P(vp)]),
         "irm_table_destroy": (ctypes.c_int, [vp]),
         "irm_table_info": (ctypes.c_int, [vp, P(u32), P(u32), P(u64), P(u32), P(sz)]),
@@ -126,6 +127,38 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _on_stream(stream):
+    """Context in which the binding allocates its temporaries: the stream the
+    kernels run on, so the caching allocator hands a freed block (say, the
+    decode workspace) only to work ordered after those kernels."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(stream)
+
+
+def check_out(out, shape, device, name: str = "out", dtype=None):
+    """Refuse a caller-supplied output the kernels could overrun: the C ABI
+    takes no size for outputs and writes exactly ``shape`` elements, so the
+    tensor must have that shape, the dtype (bfloat16 unless given), be
+    contiguous and live on ``device``."""
+    import torch
+    dtype = torch.bfloat16 if dtype is None else dtype
+    if not isinstance(out, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {out.dtype}")
+    if not out.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if out.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {out.device}")
 
 
 def rope_inv_freq(theta: float = 10000.0) -> np.ndarray:
@@ -193,7 +226,10 @@ class Table:
         inv = np.ascontiguousarray(inv_freq, dtype=np.float64)
         assert inv.shape == (32,)
         if dev_buf is None:
-            dev_buf = torch.empty(max(self.device_bytes, 256), dtype=torch.uint8, device="cuda")
+            with _on_stream(stream):
+                dev_buf = torch.empty(max(self.device_bytes, 256), dtype=torch.uint8, device="cuda")
+        elif dev_buf.dtype != torch.uint8 or not dev_buf.is_cuda or not dev_buf.is_contiguous():
+            raise ValueError("dev_buf must be a contiguous uint8 CUDA tensor")
         _check(lib().irm_table_upload(self._h, inv.ctypes.data, _ptr(dev_buf), dev_buf.numel(),
                                       _stream(stream)), "irm_table_upload")
         self._dev = dev_buf
@@ -210,8 +246,9 @@ class Table:
 
     def gather_index(self, stream=None):
         import torch
-        pr = torch.empty(self.total_rows, dtype=torch.int64, device="cuda")
-        de = torch.empty(self.total_rows, dtype=torch.int32, device="cuda")
+        with _on_stream(stream):
+            pr = torch.empty(self.total_rows, dtype=torch.int64, device="cuda")
+            de = torch.empty(self.total_rows, dtype=torch.int32, device="cuda")
         _check(lib().irm_table_gather_index(self._h, _ptr(pr), _ptr(de), _stream(stream)),
                "irm_table_gather_index")
         return pr, de
@@ -230,9 +267,11 @@ def rotate_gather(table: Table, pool, out=None, kr_f32: bool = False, stream=Non
     Returns out (bf16 [total_rows][576]) and, if kr_f32, the float rotated k_r."""
     import torch
     _bf16_2d(pool, ROW, "pool")
-    if out is None:
-        out = torch.empty((table.total_rows, ROW), dtype=torch.bfloat16, device=pool.device)
-    kr = torch.empty((table.total_rows, D_ROPE), dtype=torch.float32, device=pool.device) if kr_f32 else None
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((table.total_rows, ROW), dtype=torch.bfloat16, device=pool.device)
+        kr = torch.empty((table.total_rows, D_ROPE), dtype=torch.float32, device=pool.device) if kr_f32 else None
+    check_out(out, (table.total_rows, ROW), pool.device)
     _check(lib().irm_rotate_gather(table.handle, _ptr(pool), pool.shape[0], _ptr(out), _ptr(kr),
                                    _stream(stream)), "irm_rotate_gather")
     return (out, kr) if kr_f32 else out
@@ -256,12 +295,15 @@ def mla_decode(q_lat, q_rope, table: Table, pool, n_splits: int = 0, scale: floa
     B, H = q_lat.shape[0], q_lat.shape[1]
     if B != table.n_seq or tuple(q_rope.shape) != (B, H, D_ROPE):
         raise ValueError("q_lat/q_rope must be [n_seq][H][512] / [n_seq][H][64]")
-    if out is None:
-        out = torch.empty((B, H, D_LATENT), dtype=torch.bfloat16, device=pool.device)
-    lse = torch.empty((B, H), dtype=torch.float32, device=pool.device) if want_lse else None
     need = decode_workspace_bytes(table, H, n_splits)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=pool.device)
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((B, H, D_LATENT), dtype=torch.bfloat16, device=pool.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=pool.device) if want_lse else None
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=pool.device)
+    check_out(out, (B, H, D_LATENT), pool.device)
+    check_out(workspace, (workspace.numel(),), pool.device, "workspace", torch.uint8)
     _check(lib().irm_mla_decode(_ptr(q_lat), _ptr(q_rope), table.handle, _ptr(pool), pool.shape[0], H,
                                 n_splits, float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "irm_mla_decode")
@@ -279,9 +321,11 @@ def mla_prefill_tail(q_lat, q_rope, q_pos0: int, table: Table, pool, scale: floa
     nq, H = q_lat.shape[0], q_lat.shape[1]
     if tuple(q_rope.shape) != (nq, H, D_ROPE):
         raise ValueError("q_rope must be [n_q][H][64]")
-    if out is None:
-        out = torch.empty((nq, H, D_LATENT), dtype=torch.bfloat16, device=pool.device)
-    lse = torch.empty((nq, H), dtype=torch.float32, device=pool.device) if want_lse else None
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((nq, H, D_LATENT), dtype=torch.bfloat16, device=pool.device)
+        lse = torch.empty((nq, H), dtype=torch.float32, device=pool.device) if want_lse else None
+    check_out(out, (nq, H, D_LATENT), pool.device)
     _check(lib().irm_mla_prefill_tail(_ptr(q_lat), _ptr(q_rope), int(q_pos0), nq, table.handle, _ptr(pool),
                                       pool.shape[0], H, float(scale), _ptr(out), _ptr(lse),
                                       _stream(stream)), "irm_mla_prefill_tail")
@@ -299,9 +343,11 @@ def mla_prefill_assembled(q_lat, q_rope, q_pos0: int, kv, scale: float = DEFAULT
     nq, H = q_lat.shape[0], q_lat.shape[1]
     if tuple(q_rope.shape) != (nq, H, D_ROPE):
         raise ValueError("q_rope must be [n_q][H][64]")
-    if out is None:
-        out = torch.empty((nq, H, D_LATENT), dtype=torch.bfloat16, device=kv.device)
-    lse = torch.empty((nq, H), dtype=torch.float32, device=kv.device) if want_lse else None
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((nq, H, D_LATENT), dtype=torch.bfloat16, device=kv.device)
+        lse = torch.empty((nq, H), dtype=torch.float32, device=kv.device) if want_lse else None
+    check_out(out, (nq, H, D_LATENT), kv.device)
     _check(lib().irm_mla_prefill_assembled(_ptr(q_lat), _ptr(q_rope), int(q_pos0), nq, _ptr(kv), kv.shape[0], H,
                                            float(scale), _ptr(out), _ptr(lse), _stream(stream)),
            "irm_mla_prefill_assembled")
@@ -324,9 +370,9 @@ def mla_kv_upproj(kv, w_uk, w_uv, out=None, stream=None):
         raise ValueError("w_uk and w_uv must be [H][128][512]")
     rows = kv.shape[0]
     if out is None:
-        out = torch.empty((H, rows, D_NOPE + D_V), dtype=torch.bfloat16, device=kv.device)
-    elif tuple(out.shape) != (H, rows, D_NOPE + D_V):
-        raise ValueError("out must be [H][rows][256]")
+        with _on_stream(stream):
+            out = torch.empty((H, rows, D_NOPE + D_V), dtype=torch.bfloat16, device=kv.device)
+    check_out(out, (H, rows, D_NOPE + D_V), kv.device)
     _check(lib().irm_mla_kv_upproj(_ptr(kv), rows, _ptr(w_uk), _ptr(w_uv), H, _ptr(out), _stream(stream)),
            "irm_mla_kv_upproj")
     return out
@@ -346,9 +392,11 @@ def mla_prefill_nonabsorbed(q_nope, q_rope, q_pos0: int, kv, kvh, scale: float =
         raise ValueError("q_rope must be [n_q][H][64]")
     if tuple(kvh.shape) != (H, kv.shape[0], D_NOPE + D_V):
         raise ValueError("kvh must be [H][rows][256] for the rows of kv")
-    if out is None:
-        out = torch.empty((nq, H, D_V), dtype=torch.bfloat16, device=kv.device)
-    lse = torch.empty((nq, H), dtype=torch.float32, device=kv.device) if want_lse else None
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((nq, H, D_V), dtype=torch.bfloat16, device=kv.device)
+        lse = torch.empty((nq, H), dtype=torch.float32, device=kv.device) if want_lse else None
+    check_out(out, (nq, H, D_V), kv.device)
     _check(lib().irm_mla_prefill_nonabsorbed(_ptr(q_nope), _ptr(q_rope), int(q_pos0), nq, _ptr(kv), _ptr(kvh),
                                              kv.shape[0], H, float(scale), _ptr(out), _ptr(lse), _stream(stream)),
            "irm_mla_prefill_nonabsorbed")
@@ -356,9 +404,11 @@ def mla_prefill_nonabsorbed(q_nope, q_rope, q_pos0: int, kv, kvh, scale: float =
 
 
 def gqa_inv_freq(theta: float, head_dim: int) -> np.ndarray:
-    """theta^(-2i/head_dim), i < head_dim/2 (plain RoPE frequencies of a GQA head)."""
-    i = np.arange(head_dim // 2, dtype=np.float64)
-    return theta ** (-2.0 * i / head_dim)
+    """theta^(-2i/head_dim), i < head_dim/2 (plain RoPE frequencies of a GQA
+    head), computed by the library."""
+    out = np.zeros(max(1, head_dim // 2), dtype=np.float64)
+    _check(lib().irm_rope_inv_freq_dim(float(theta), int(head_dim), out.ctypes.data), "irm_rope_inv_freq_dim")
+    return out
 
 
 def gqa_rotate_gather(table: Table, pool, n_kv_heads: int, head_dim: int, inv_freq, out=None, stream=None):
@@ -370,11 +420,13 @@ def gqa_rotate_gather(table: Table, pool, n_kv_heads: int, head_dim: int, inv_fr
     inv = np.ascontiguousarray(inv_freq, dtype=np.float64)
     if inv.size != head_dim // 2:
         raise ValueError("inv_freq must hold head_dim / 2 values")
-    if out is None:
-        out = torch.empty((table.total_rows, width), dtype=torch.bfloat16, device=pool.device)
     nb = ctypes.c_size_t()
     _check(lib().irm_gqa_workspace(table.handle, head_dim, ctypes.byref(nb)), "irm_gqa_workspace")
-    ws = torch.empty(max(16, nb.value), dtype=torch.uint8, device=pool.device)
+    with _on_stream(stream):
+        if out is None:
+            out = torch.empty((table.total_rows, width), dtype=torch.bfloat16, device=pool.device)
+        ws = torch.empty(max(16, nb.value), dtype=torch.uint8, device=pool.device)
+    check_out(out, (table.total_rows, width), pool.device)
     _check(lib().irm_gqa_rotate_gather(table.handle, _ptr(pool), pool.shape[0], n_kv_heads, head_dim,
                                        inv.ctypes.data, _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
            "irm_gqa_rotate_gather")

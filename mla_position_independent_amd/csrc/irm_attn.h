@@ -41,22 +41,18 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   return v;
 }
 
-// Wave-wide copy: lane l's 16 bytes at g land at LDS address lds + 16 l
-// (one wait state between the M0 write and the LDS-DMA load).
+// Wave-wide copy: lane l's 16 bytes at g land at LDS address lds + 16 l.
+// The compiler writes M0 (an input operand of the asm) right before it; the
+// s_nop gives the one wait state between that write and the LDS-DMA load.
 // kStream marks data read exactly once (the non-temporal policy keeps it
 // from displacing rows that other workgroups still read from the caches).
 template <bool kStream = false>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
   if constexpr (kStream)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :
-                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "{m0}"(m0));
   else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-                 : "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m0));
 }
 
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

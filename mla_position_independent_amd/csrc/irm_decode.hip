@@ -330,6 +330,7 @@ StreamArgs stream_args(const irm_table* t, const void* pool, uint64_t pool_rows)
 uint32_t decode_default_splits(const irm_table* t, uint32_t n_groups) {
   // one workgroup per CU (256 CUs) with >= 256 rows per split; a workgroup
   // covers four head groups when the head count allows it
+  if (t->n_seq == 0 || n_groups == 0) return 1;  // an empty batch has nothing to split
   const uint32_t units = (n_groups % 4 == 0) ? n_groups / 4 : n_groups;
   const uint32_t want = (256 + t->n_seq * units - 1) / (t->n_seq * units);
   const uint32_t cap = (t->max_seq_len + 255) / 256;

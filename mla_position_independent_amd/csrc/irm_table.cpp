@@ -42,6 +42,16 @@ extern "C" irm_status irm_rope_inv_freq(double theta, double* inv_freq) {
   return IRM_OK;
 }
 
+extern "C" irm_status irm_rope_inv_freq_dim(double theta, uint32_t dim, double* inv_freq) {
+  if (!inv_freq) return fail(IRM_EINVAL, "irm_rope_inv_freq_dim: inv_freq is NULL");
+  if (!(theta > 1.0) || !std::isfinite(theta))
+    return fail(IRM_EINVAL, "irm_rope_inv_freq_dim: theta must be finite and > 1");
+  if (dim < 2 || dim % 2 != 0 || dim > 4096)
+    return fail(IRM_EINVAL, "irm_rope_inv_freq_dim: dim must be even, in [2, 4096]");
+  for (uint32_t i = 0; i < dim / 2; ++i) inv_freq[i] = std::pow(theta, -2.0 * (double)i / (double)dim);
+  return IRM_OK;
+}
+
 extern "C" irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunks,
                                        const uint32_t* seq_first, uint32_t n_seq,
                                        uint64_t pool_rows, irm_table** out) {

@@ -235,3 +235,56 @@ def test_table_builder_agrees_with_oracle_on_generated_tables(case):
         with pytest.raises(irm.IrmError) as e:
             irm.Table(c, sf, _POOL)
         assert e.value.code == ocode
+
+
+def test_rope_inv_freq_dim_matches_oracle():
+    from oracle import irm_gqa
+    for d in (2, 16, 48, 64, 128, 256):
+        got = irm.gqa_inv_freq(10000.0, d)        # the library's irm_rope_inv_freq_dim
+        want = irm_gqa.gqa_inv_freq(10000.0, d)
+        assert got.shape == (d // 2,)
+        assert np.allclose(got, want, rtol=1e-15, atol=0)
+    # the 64-wide form is the k_r frequencies of irm_rope_inv_freq, bit for bit
+    assert np.array_equal(irm.gqa_inv_freq(10000.0, 64), irm.rope_inv_freq(10000.0))
+    for theta, d in ((0.5, 64), (10000.0, 63), (10000.0, 0), (float("inf"), 64), (10000.0, 8192)):
+        with pytest.raises(irm.IrmError) as e:
+            irm.gqa_inv_freq(theta, d)
+        assert e.value.code == "EINVAL"
+
+
+def test_decode_workspace_of_an_empty_batch():
+    # a table without sequences is legal; asking for its decode workspace must
+    # not divide by the sequence count (run apart: a host fault would end the run)
+    import subprocess
+    import sys
+    code = ("import numpy as np, mla_position_independent_amd as irm\n"
+            "t = irm.Table(np.zeros(0, irm.CHUNK_DTYPE), np.array([0], np.uint32), 0)\n"
+            "assert t.n_seq == 0\n"
+            "for h in (16, 64, 128):\n"
+            "    assert irm.decode_workspace_bytes(t, h) <= 512\n"
+            "print('ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip() == "ok"
+
+
+def test_check_out_refuses_outputs_the_kernels_could_overrun():
+    import torch
+    good = torch.empty((3, 4), dtype=torch.bfloat16)
+    irm.check_out(good, (3, 4), "cpu")
+    with pytest.raises(ValueError):
+        irm.check_out(torch.empty((3, 5), dtype=torch.bfloat16), (3, 4), "cpu")
+    with pytest.raises(ValueError):
+        irm.check_out(torch.empty((12,), dtype=torch.bfloat16), (3, 4), "cpu")
+    with pytest.raises(TypeError):
+        irm.check_out(torch.empty((3, 4), dtype=torch.float32), (3, 4), "cpu")
+    with pytest.raises(TypeError):
+        irm.check_out(torch.empty((3, 4), dtype=torch.int16), (3, 4), "cpu")
+    with pytest.raises(ValueError):
+        irm.check_out(torch.empty((4, 3), dtype=torch.bfloat16).t(), (3, 4), "cpu")
+    with pytest.raises(ValueError):
+        irm.check_out(good, (3, 4), "meta")
+    with pytest.raises(TypeError):
+        irm.check_out(np.zeros((3, 4)), (3, 4), "cpu")
+    irm.check_out(torch.empty(10, dtype=torch.uint8), (10,), "cpu", "workspace", torch.uint8)
