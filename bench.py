@@ -131,22 +131,95 @@ def ingest_counters(key: str, fetch_dir: str, write_dir: str, cal_fetch_dir: str
     log(f"{key}: fetch {fetch / 1e6:.1f} MB, write {write / 1e6:.1f} MB per launch -> {TRAFFIC_FILE}")
 
 
+class ClockSampler:
+    """Samples the GPU's shader clock from sysfs on a host thread while a leg
+    runs (the part lowers its clock under sustained load, so MFMA-bound
+    rates depend on it).  Reads the current level of pp_dpm_sclk or the
+    hwmon sclk input of the first amdgpu card that has one; reports nothing
+    where neither exists."""
+
+    def __init__(self, period_s: float = 0.002):
+        import glob
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.source = None
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            for cand in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "freq1_input"))):
+                label = os.path.join(os.path.dirname(cand), "freq1_label")
+                try:
+                    if open(label).read().strip().lower() == "sclk":
+                        self.source = ("hwmon", cand)
+                        break
+                except OSError:
+                    pass
+            if self.source is None and os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                self.source = ("dpm", os.path.join(dev, "pp_dpm_sclk"))
+            if self.source is not None:
+                break
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        kind, path = self.source
+        with open(path) as f:
+            txt = f.read()
+        if kind == "hwmon":
+            return int(txt.strip()) / 1e6
+        for line in txt.splitlines():
+            if line.strip().endswith("*"):
+                tok = line.split(":", 1)[1].strip().split()[0].lower()
+                return float(tok.replace("mhz", ""))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except (OSError, ValueError, IndexError):
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.source is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.source is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                "source": self.source[0]}
+
+
 def time_leg(fn, steps: int, warmup: int, inner_events: bool = True):
     """Run fn(ev_mid_or_None) warmup+steps times.  Returns wall ms per step
-    (synchronised on both sides of the timed region) and the mean event time
-    of the part fn brackets (ms)."""
+    (synchronised on both sides of the timed region), the median event time
+    of the part fn brackets (ms), the mean of those event times, and the
+    shader clock sampled during the timed region."""
     import torch
     for _ in range(warmup):
         fn(None)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for k in range(steps):
-        fn(evs[k] if inner_events else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kern = [a.elapsed_time(b) for a, b in evs] if inner_events else []
-    return (t1 - t0) * 1e3 / steps, (sum(kern) / len(kern)) if kern else None
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for k in range(steps):
+            fn(evs[k] if inner_events else None)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    kern = sorted(a.elapsed_time(b) for a, b in evs) if inner_events else []
+    med = kern[len(kern) // 2] if kern else None
+    mean = sum(kern) / len(kern) if kern else None
+    return (t1 - t0) * 1e3 / steps, med, mean, clk.summary()
 
 
 _SCRUB = []
@@ -173,44 +246,103 @@ def time_cold(fn, n: int = 5):
     return ts[len(ts) // 2]
 
 
-def leg_gather(args, irm, torch, synth):
-    log("rotate-gather: generating 64 x 32768-token batch")
-    w = synth.rotate_gather_batch()
+def time_events(fn, n: int = 10):
+    """Median event time (ms) of fn over n back-to-back calls, after one
+    untimed call."""
+    import torch
+    fn()
+    ts = []
+    for _ in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
+    """One step = the per-batch device work of a new chunk table on the
+    rotate-gather batch: the row-map and trig passes (irm_table_prepare) and
+    the rotate-gather kernel, with the table's image and the pool in HBM."""
+    log(f"{label}: generating 64 x 32768-token batch")
+    w = (make or synth.rotate_gather_batch)()
     pool = irm.to_device_bf16(w.pool)
     inv = irm.rope_inv_freq(w.theta)
     t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0]).upload(inv)
     out = torch.empty((t.total_rows, 576), dtype=torch.bfloat16, device="cuda")
 
     def step(ev):
-        t.set_rope(inv)                     # per-entry trig (double sincos)
+        t.prepare(inv)                      # row map + per-entry trig (double sincos)
         if ev is not None:
             ev[0].record()
         irm.rotate_gather(t, pool, out=out)
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, kern_mean, clk = time_leg(step, args.steps, args.warmup)
     tokens = t.total_rows
     alg_bytes = 2 * ROW_BYTES * tokens
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic("rotate_gather_kernel")
+    traffic = measured_traffic("rotate_gather_kernel" + ("" if make is None else ":" + w.name))
     cold_ms = time_cold(lambda: irm.rotate_gather(t, pool, out=out))
-    log(f"rotate-gather: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms, {achieved:.0f} GB/s; "
-        f"after a cache scrub {cold_ms:.3f} ms")
+    prep_ms = time_events(lambda: t.prepare(inv))
+    upload_ms = time_events(lambda: t.upload(inv, dev_buf=t._dev))
+    log(f"{label}: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms (median), {achieved:.0f} GB/s; "
+        f"after a cache scrub {cold_ms:.3f} ms; prepare {prep_ms:.3f} ms, upload with its copy {upload_ms:.3f} ms")
     res = {
-        "tokens": tokens, "ms_per_step": ms, "kernel_ms": kern_ms,
+        "tokens": tokens, "ms_per_step": ms, "kernel_ms": kern_ms, "entries": int(t.n_chunks),
+        "mean_entry_len": round(tokens / max(1, t.n_chunks), 1),
+        "table_prepare_ms": round(prep_ms, 4),
+        "table_upload_ms": round(upload_ms, 4),
+        # the host image copied by the upload: everything before the trig and
+        # row-map regions, which the device passes write (256-byte aligned regions)
+        "table_h2d_bytes": int(t.device_bytes - 256 * t.n_chunks - -(-16 * (t.total_rows + 64) // 256) * 256),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "rotate_gather_kernel",
+                     "kernel_ms_median": round(kern_ms, 4), "kernel_ms_mean": round(kern_mean, 4),
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "cold_cache_kernel_ms": round(cold_ms, 4),
                      "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "sclk": clk,
         "workload": w, "table": t,
     }
     return res
 
 
+def leg_gather_cdc(args, irm, torch, synth):
+    """The rotate-gather batch with CDC-like chunk lengths (mean ~127 instead
+    of 272): about twice the entries, the harder per-entry case."""
+    r = leg_gather(args, irm, torch, synth, make=synth.rotate_gather_cdc_batch, label="rotate-gather (CDC lengths)")
+    w = r.pop("workload")
+    r.pop("table")
+    r["workload"] = w.name
+    r["value"] = round(r["tokens"] / (r["ms_per_step"] * 1e-3), 1)
+    r["unit"] = "assembled KV tokens/s"
+    return r
+
+
+def _delta0_chunks(chunks):
+    """The same entries with every delta 0 (p_src = p_tgt): the same pool
+    rows, read through the same row map, with nothing to rotate."""
+    c = chunks.copy()
+    c["p_src"] = c["p_tgt"]
+    return c
+
+
 def leg_decode(args, irm, torch, synth, name, make):
+    """One call = the split pass and the combine pass over the batch, the
+    table prepared once (a decode loop reuses a sequence's table every step).
+    Besides the call itself (rows gathered through the chunk table, k_r
+    rotated on load), the same batch is decoded twice more to price the
+    rotation: over the same rows with every delta set to 0 (same row map and
+    scattered rows, nothing rotated), and over the cache assembled by
+    rotate-gather beforehand, as one fresh entry per sequence (contiguous
+    rows, nothing rotated)."""
+    import numpy as np
     log(f"{name}: generating")
     w = make()
     pool = irm.to_device_bf16(w.pool)
@@ -220,15 +352,38 @@ def leg_decode(args, irm, torch, synth, name, make):
     out = torch.empty((w.n_seq, H, 512), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(irm.decode_workspace_bytes(t, H, w.n_splits), dtype=torch.uint8, device="cuda")
 
+    def call(table, kv):
+        irm.mla_decode(ql, qr, table, kv, n_splits=w.n_splits, scale=w.scale, out=out, workspace=ws)
+
     def step(ev):
         if ev is not None:
             ev[0].record()
-        irm.mla_decode(ql, qr, t, pool, n_splits=w.n_splits, scale=w.scale, out=out, workspace=ws)
+        call(t, pool)
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, kern_mean, clk = time_leg(step, args.steps, args.warmup)
     cold_ms = time_cold(lambda: step(None))
+
+    # the price of the rotation on load
+    t0 = irm.Table(_delta0_chunks(w.chunks), w.seq_first, w.pool.shape[0]).upload(irm.rope_inv_freq(w.theta))
+    assembled = irm.rotate_gather(t, pool)
+    base = t.seq_base()
+    rows = [(int(base[s]), int(base[s + 1] - base[s]), 0, 0, 1) for s in range(t.n_seq)]
+    tf = irm.Table(np.array(rows, irm.CHUNK_DTYPE), np.arange(t.n_seq + 1, dtype=np.uint32), t.total_rows).upload()
+    torch.cuda.synchronize()
+    variants = {}
+    for rnd in range(3):     # interleaved rounds: the clock drifts with the chip's temperature
+        for key, tab, kv in (("rotate_on_load", t, pool), ("same_rows_delta0", t0, pool),
+                             ("assembled_contiguous", tf, assembled)):
+            variants.setdefault(key, []).append(time_events(lambda: call(tab, kv), 10))
+    rot = {k: round(sorted(v)[1], 4) for k, v in variants.items()}
+    rot["rotation_cost_frac"] = round(rot["rotate_on_load"] / rot["same_rows_delta0"] - 1.0, 4)
+    rot["table_and_gather_cost_frac"] = round(rot["rotate_on_load"] / rot["assembled_contiguous"] - 1.0, 4)
+    rot["method"] = ("median of 10 back-to-back calls per variant, middle of 3 interleaved rounds; "
+                     "same_rows_delta0 = the same entries with p_src = p_tgt")
+    del assembled, tf, t0
+
     # the split pass runs one 16-head group per workgroup unless the head
     # count is a multiple of 64 (four groups share every KV tile)
     kernel = "decode_shared_kernel" if H % 64 == 0 else "decode_private_kernel"
@@ -237,8 +392,8 @@ def leg_decode(args, irm, torch, synth, name, make):
     alg_bytes = kv + qo
     flops = 2 * (576 + 512) * H * t.total_rows
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"{name}: {kern_ms:.3f} ms/call, {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s; "
-        f"after a cache scrub {cold_ms:.3f} ms")
+    log(f"{name}: {kern_ms:.3f} ms/call (median), {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s; "
+        f"after a cache scrub {cold_ms:.3f} ms; rotation {rot}")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"{name}: oracle on a sample of the batch")
@@ -250,10 +405,14 @@ def leg_decode(args, irm, torch, synth, name, make):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(kernel + ":" + w.name),
                      "kernel": kernel + " + decode_combine_kernel",
+                     "kernel_ms_median": round(kern_ms, 4), "kernel_ms_mean": round(kern_mean, 4),
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "cold_cache_kernel_ms": round(cold_ms, 4),
                      "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+        "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "rotation_on_load": rot,
+        "sclk": clk,
     }
 
 
@@ -274,7 +433,7 @@ def leg_tiny(args, irm, torch, synth):
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, _, _ = time_leg(step, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -323,12 +482,12 @@ def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = T
         if ev is not None:
             ev[1].record()
 
-    n_steps, n_warm = max(2, args.steps // 4), min(args.warmup, 2)
+    n_steps, n_warm = max(3, args.steps // 4), min(args.warmup, 2)
     if not assembled:   # profiling the fused kernel alone
-        _, fused_ms = time_leg(fused_call, n_steps, n_warm)
+        fused_ms = time_leg(fused_call, n_steps, n_warm)[1]
         log(f"tail-prefill, rotation on load in one kernel: {fused_ms:.3f} ms")
         return None
-    ms, kern_ms = time_leg(step, n_steps, n_warm)
+    ms, kern_ms, kern_mean, clk = time_leg(step, n_steps, n_warm)
     fused_ms = time_leg(fused_call, n_steps, 1)[1] if fused else None
     pairs = nq * w.q_pos0 + nq * (nq + 1) // 2      # visible (query, key) pairs
     flops = pairs * H * 2 * (576 + 512)
@@ -349,7 +508,10 @@ def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = T
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
                      "traffic": measured_traffic("prefill_kernel"), "kernel": "prefill_kernel (assembled cache)",
-                     "algorithmic_flops_per_launch": flops},
+                     "kernel_ms_median": round(kern_ms, 4), "kernel_ms_mean": round(kern_mean, 4),
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": ROW_BYTES * t.total_rows + nq * H * (576 + 512) * 2},
+        "sclk": clk,
     }
 
 
@@ -385,9 +547,9 @@ def leg_nonabsorbed(args, irm, torch, synth):
         if ev is not None:
             ev[1].record()
 
-    n_steps = max(2, args.steps // 2)
-    _, up_ms = time_leg(up, n_steps, min(args.warmup, 2))
-    _, kern_ms = time_leg(attend, n_steps, min(args.warmup, 2))
+    n_steps = max(3, args.steps // 2)
+    up_ms = time_leg(up, n_steps, min(args.warmup, 2))[1]
+    _, kern_ms, _, clk = time_leg(attend, n_steps, min(args.warmup, 2))
     pairs = nq * w.q_pos0 + nq * (nq + 1) // 2
     flops = pairs * H * 2 * (192 + 128)
     up_flops = 2 * kv.shape[0] * 512 * 256 * H
@@ -403,6 +565,7 @@ def leg_nonabsorbed(args, irm, torch, synth):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
                      "traffic": measured_traffic("mha_prefill_kernel"), "kernel": "mha_prefill_kernel",
                      "algorithmic_flops_per_launch": flops},
+        "sclk": clk,
     }
 
 
@@ -428,7 +591,7 @@ def leg_gqa(args, irm, torch, gather):
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, _, _ = time_leg(step, args.steps, args.warmup)
     tokens = t.total_rows
     alg_bytes = 2 * 2 * width * tokens
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
@@ -609,7 +772,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="gather,tiny,decode,long_decode,prefill,nonabsorbed,gqa,producer",
+    ap.add_argument("--legs", default="gather,gather_cdc,tiny,decode,long_decode,prefill,nonabsorbed,gqa,producer",
                     help="comma list; without gather only the named legs run (profiling, no JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-seconds-legs", type=float, default=5.0,
@@ -659,6 +822,8 @@ def main():
         for name in legs:
             if name == "gather":
                 g = leg_gather(args, irm, torch, synth)
+            elif name == "gather_cdc":
+                leg_gather_cdc(args, irm, torch, synth)
             elif name == "tiny":
                 leg_tiny(args, irm, torch, synth)
             elif name == "decode":
@@ -678,6 +843,8 @@ def main():
         return
     g = leg_gather(args, irm, torch, synth)
     extra = {}
+    if "gather_cdc" in legs:
+        extra["gather_cdc"] = leg_gather_cdc(args, irm, torch, synth)
     if "tiny" in legs:
         extra["tiny_decode"] = leg_tiny(args, irm, torch, synth)
     if "decode" in legs:
@@ -715,7 +882,12 @@ def main():
         "config": {"workload": w.name, "requests": w.n_seq, "tokens_per_request": 32768,
                    "registry_chunks": w.meta["n_registry"], "chunk_len": "uniform[32,512]",
                    "hit_fraction_by_entry": 0.8, "p_src_range": [0, 131072], "row": "576 x bf16",
-                   "step": "per-entry trig pass + rotate-gather, table and pool resident in HBM"},
+                   "step": "per-batch device passes of the chunk table (row map + per-entry trig) + rotate-gather, "
+                           "the table's image and the pool resident in HBM"},
+        "table_prepare_ms": g["table_prepare_ms"],
+        "table_upload_ms": g["table_upload_ms"],
+        "table_h2d_bytes": g["table_h2d_bytes"],
+        "sclk": g["sclk"],
         "roofline": g["roofline"],
         "cpu_baseline": cpu,
         "legs": extra,

@@ -167,6 +167,18 @@ irm_status irm_table_upload(irm_table* t, const double* inv_freq, void* dev_buf,
                             size_t dev_bytes, void* stream);
 
 /*
+ * The device passes of irm_table_upload without its host-to-device copy: on
+ * `stream`, rebuild the row map (one record per assembled row: pool row,
+ * delta, entry) from the entries already in the uploaded device image, then
+ * the per-entry cos/sin of delta * inv_freq[i] (as irm_table_set_rope).
+ * host inv_freq[32].  Requires an uploaded table (EINVAL otherwise); the
+ * result is the same as that of irm_table_upload.  This is the per-batch
+ * device work of a table whose image reached HBM by a copy made earlier or
+ * on another stream.
+ */
+irm_status irm_table_prepare(irm_table* t, const double* inv_freq, void* stream);
+
+/*
  * Recompute, on `stream`, the per-entry cos/sin of delta * inv_freq[i] of an
  * uploaded table (the trig pass irm_table_upload also runs), e.g. for another
  * model's rotary frequencies.  host inv_freq[32].  No host-to-device copy.

@@ -34,7 +34,7 @@ CHUNK_DTYPE = np.dtype(
 EXPORTS = (
     "irm_last_error", "irm_rope_inv_freq", "irm_rope_inv_freq_dim", "irm_table_create", "irm_table_destroy",
     "irm_table_info", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
-    "irm_table_set_rope",
+    "irm_table_set_rope", "irm_table_prepare",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
     "irm_mla_decode", "irm_mla_prefill_tail", "irm_mla_prefill_assembled", "irm_gqa_workspace",
     "irm_gqa_rotate_gather", "irm_mla_kv_upproj", "irm_mla_prefill_nonabsorbed",
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "irm_table_expand_host": (ctypes.c_int, [vp, vp, vp, vp]),
         "irm_table_upload": (ctypes.c_int, [vp, vp, vp, sz, vp]),
         "irm_table_set_rope": (ctypes.c_int, [vp, vp, vp]),
+        "irm_table_prepare": (ctypes.c_int, [vp, vp, vp]),
         "irm_table_gather_index": (ctypes.c_int, [vp, vp, vp, vp]),
         "irm_rotate_gather": (ctypes.c_int, [vp, vp, u64, vp, vp, vp]),
         "irm_mla_decode_workspace": (ctypes.c_int, [vp, u32, u32, P(sz)]),
@@ -233,6 +234,15 @@ class Table:
         _check(lib().irm_table_upload(self._h, inv.ctypes.data, _ptr(dev_buf), dev_buf.numel(),
                                       _stream(stream)), "irm_table_upload")
         self._dev = dev_buf
+        self._inv = inv
+        return self
+
+    def prepare(self, inv_freq: Optional[np.ndarray] = None, stream=None) -> "Table":
+        """Rebuild the row map and the per-entry cos/sin of the uploaded image
+        on the GPU (the device passes of upload(), without its copy)."""
+        inv = self._inv if inv_freq is None else np.ascontiguousarray(inv_freq, dtype=np.float64)
+        assert inv.shape == (32,)
+        _check(lib().irm_table_prepare(self._h, inv.ctypes.data, _stream(stream)), "irm_table_prepare")
         self._inv = inv
         return self
 

@@ -90,11 +90,21 @@ extern "C" irm_status irm_table_upload(irm_table* t, const double* inv_freq, voi
                  "irm_table_upload: hipMemcpyAsync");
   if (st != IRM_OK) return st;
   t->dev = dev_buf;
-  st = irm::launch_rowmap(t, s);
-  if (st != IRM_OK) { t->dev = nullptr; return st; }
-  st = irm_table_set_rope(t, inv_freq, stream);
+  st = irm_table_prepare(t, inv_freq, stream);
   if (st != IRM_OK) t->dev = nullptr;
   return st;
+}
+
+extern "C" irm_status irm_table_prepare(irm_table* t, const double* inv_freq, void* stream) {
+  irm_status st = need_uploaded(t, "irm_table_prepare");
+  if (st != IRM_OK) return st;
+  if (!inv_freq) return fail(IRM_EINVAL, "irm_table_prepare: inv_freq is NULL");
+  for (int i = 0; i < (int)irm::kPairs; ++i)
+    if (!std::isfinite(inv_freq[i])) return fail(IRM_EINVAL, "irm_table_prepare: inv_freq not finite");
+  if ((st = check_device()) != IRM_OK) return st;
+  st = irm::launch_rowmap(t, static_cast<hipStream_t>(stream));
+  if (st != IRM_OK) return st;
+  return irm_table_set_rope(t, inv_freq, stream);
 }
 
 extern "C" irm_status irm_table_set_rope(irm_table* t, const double* inv_freq, void* stream) {

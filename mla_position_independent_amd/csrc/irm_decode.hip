@@ -365,6 +365,16 @@ static uint32_t splits_per_workgroup(uint32_t n_seq, uint32_t n_splits, uint32_t
   return best;
 }
 
+// Consecutive splits one workgroup streams (1 for the 16-head-group kernel).
+static uint32_t splits_per_wg_of(const irm_table* t, uint32_t n_heads, uint32_t n_splits) {
+  const uint32_t G = n_heads / 16;
+  return G % kSplitGroups == 0 ? splits_per_workgroup(t->n_seq, n_splits, G / kSplitGroups) : 1;
+}
+
+uint32_t decode_parts(const irm_table* t, uint32_t n_heads, uint32_t n_splits) {
+  return n_splits / splits_per_wg_of(t, n_heads, n_splits);
+}
+
 irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_rope, const void* pool,
                          uint64_t pool_rows, uint32_t n_heads, uint32_t n_splits, float scale, void* out,
                          float* lse, float* ws_acc, float* ws_ml, hipStream_t s) {
@@ -383,7 +393,7 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
   a.scale_log2 = scale * kLog2e;
   for (int i = 0; i < (int)kPairs; ++i) a.f.w[i] = t->inv_freq[i];
   const bool shared = G % kSplitGroups == 0;
-  a.splits_per_wg = shared ? splits_per_workgroup(t->n_seq, n_splits, G / kSplitGroups) : 1;
+  a.splits_per_wg = splits_per_wg_of(t, n_heads, n_splits);
   const uint64_t bs = (uint64_t)t->n_seq * (n_splits / a.splits_per_wg);
   const uint64_t grid = (bs + 7) / 8 * 8 * (shared ? G / kSplitGroups : G);
   if (grid > 0x7fffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_decode: grid too large");

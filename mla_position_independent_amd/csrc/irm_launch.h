@@ -22,6 +22,10 @@ irm_status launch_rotate_gather(const irm_table* t, const void* pool, void* out_
 // irm_decode.hip: split count used when the caller passes 0, and the launch
 // of both decode passes into a workspace laid out as [acc | ml].
 uint32_t decode_default_splits(const irm_table* t, uint32_t n_groups);
+// Partial states per sequence the split pass writes for n_splits splits (the
+// 64-head kernel merges runs of splits when the device has fewer compute
+// units than (sequence, split, head block) triples).
+uint32_t decode_parts(const irm_table* t, uint32_t n_heads, uint32_t n_splits);
 irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_rope, const void* pool,
                          uint64_t pool_rows, uint32_t n_heads, uint32_t n_splits, float scale, void* out,
                          float* lse, float* ws_acc, float* ws_ml, hipStream_t s);

@@ -18,6 +18,7 @@ from .workloads import (  # noqa: F401
     random_table,
     tiny_decode,
     rotate_gather_batch,
+    rotate_gather_cdc_batch,
     batched_decode,
     long_decode,
     tail_prefill,

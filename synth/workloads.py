@@ -249,6 +249,20 @@ def rotate_gather_batch(seed: int = 1002, n_req: int = 64, req_len: int = 32768,
                     meta={"n_registry": n_registry, "registry_rows": int(reg_len.sum())})
 
 
+def rotate_gather_cdc_batch(seed: int = 1012, n_req: int = 64, req_len: int = 32768,
+                            n_registry: int = 4096) -> Workload:
+    """The rotate-gather batch with CDC-like chunk lengths instead of uniform
+    ones: 32 plus a geometric tail (a memoryless content-defined boundary after
+    the 32-token minimum), clamped at 512, mean about 127 -- the chunk size the
+    pages' CDC targets.  About twice as many entries per request as the
+    uniform [32, 512] law (mean 272), so the per-entry work weighs more."""
+    w = rotate_gather_batch(seed=seed, n_req=n_req, req_len=req_len, n_registry=n_registry,
+                            len_fn=_cdc_like_len)
+    w.name = f"rotate_gather_cdc_{n_req}x{req_len}"
+    w.meta["chunk_len"] = "32 + Geometric(1/96) - 1, at most 512 (mean ~127)"
+    return w
+
+
 def batched_decode(seed: int = 1003, batch: int = 64, ctx: int = 8192, heads: int = 16,
                    n_splits: int = 0) -> Workload:
     """Per sequence: about 1/3 exact prefix (delta 0, rows 0..31 fresh), then
@@ -372,6 +386,7 @@ def token_requests(seed: int = 1006, n_req: int = 64, req_len: int = 32768, n_do
 WORKLOADS = {
     "tiny_decode": tiny_decode,
     "rotate_gather": rotate_gather_batch,
+    "rotate_gather_cdc": rotate_gather_cdc_batch,
     "batched_decode": batched_decode,
     "long_decode": long_decode,
     "tail_prefill": tail_prefill,

@@ -8,3 +8,10 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_runtest_logreport(report):
+    # progress reaches a pipe as each test ends (long GPU suites are watched
+    # for silence)
+    if report.when == "teardown":
+        sys.stdout.flush()

@@ -17,7 +17,7 @@ import pytest
 
 import mla_position_independent_amd as irm
 import oracle
-from synth import (CHUNK_DTYPE, FRESH, random_table, tiny_decode, rotate_gather_batch,
+from synth import (CHUNK_DTYPE, FRESH, random_table, tiny_decode, rotate_gather_batch, rotate_gather_cdc_batch,
                    batched_decode, long_decode, tail_prefill, nonabsorbed_inputs)
 from oracle import irm_nonabsorbed as NA
 
@@ -58,6 +58,17 @@ def _bf16_ulp(x):
     return np.exp2(e - 7)
 
 
+def _kr_bound(k_ref, kr_base_bits):
+    """Bound on |bf16 rotated k_r - exact| per element: one bf16 ulp of the
+    exact value (RNE, with slack), plus 2^-21 (|x| + |y|) of the element's
+    pair (x, y): the float cos/sin and the float product and fma each round
+    at 2^-24 relative to their operands, which dominates where the turned
+    value cancels toward zero (the same bound as the GQA comparison path)."""
+    kb = np.abs(oracle.bf16_to_f64(kr_base_bits))
+    pair = np.repeat(kb[:, 0::2] + kb[:, 1::2], 2, axis=1)
+    return _bf16_ulp(k_ref) * 1.0000001 + 2.0 ** -21 * pair
+
+
 # ---------------------------------------------------------------- rotate-gather
 def _check_gather(w, out_bits, kr, rows=None):
     """Compare assembled rows (all, or the given global rows) with the oracle."""
@@ -79,7 +90,7 @@ def _check_gather(w, out_bits, kr, rows=None):
         assert rel_l2(kr.astype(np.float64), k_ref) <= KR_TOL
         assert np.array_equal(kr[same].astype(np.float64), k_ref[same])
     got = oracle.bf16_to_f64(out_bits[:, 512:])
-    assert np.all(np.abs(got - k_ref) <= _bf16_ulp(k_ref) * 1.0000001)
+    assert np.all(np.abs(got - k_ref) <= _kr_bound(k_ref, w.pool[g, 512:]))
     return gather, delta
 
 
@@ -139,36 +150,64 @@ def test_rotate_gather_custom_inv_freq():
     assert rel_l2(kr.cpu().numpy().astype(np.float64), k_ref) <= KR_TOL
 
 
-def test_rotate_gather_full_size_sampled():
-    """64 requests x 32768 tokens over a 4096-chunk registry (the benchmarked
-    launch); gather map bit-exact everywhere, rows sampled against the oracle."""
-    w = rotate_gather_batch()
+def _check_gather_every_row(w):
+    """Launch the rotate-gather of a whole batch as the benchmark does and
+    compare every assembled row with the oracle, request by request: gather
+    map and deltas bit-exact, c_KV and unrotated k_r bytes bit-exact, the
+    float rotated k_r within the relative L2 bar per request and overall, the
+    bf16 k_r within one bf16 ulp of the exact value; a second launch gives the
+    same bytes."""
+    import torch
     pool = irm.to_device_bf16(w.pool)
     t = _table(w)
     out, kr = irm.rotate_gather(t, pool, kr_f32=True)
+    out2 = irm.rotate_gather(t, pool)
     pr, de = t.gather_index()
     _sync()
+    same_bytes = bool(torch.equal(out.view(torch.int16), out2.view(torch.int16)))
+    del out2
+    assert same_bytes, "two launches of the same table differ"
     exp = oracle.expand_table(w.chunks, w.seq_first, w.pool.shape[0])
     gather = np.concatenate([g for g, _, _ in exp]); delta = np.concatenate([d for _, d, _ in exp])
     assert np.array_equal(pr.cpu().numpy(), gather)
     assert np.array_equal(de.cpu().numpy().astype(np.int64), delta)
-    rng = np.random.default_rng(0)
-    rows = np.sort(np.concatenate([rng.choice(gather.shape[0], 16384, replace=False),
-                                   [0, 31, 32, gather.shape[0] - 1]]))
-    import torch
-    idx = torch.from_numpy(rows).cuda()
-    ob = irm.from_device_bf16(out.index_select(0, idx))
-    krs = kr.index_select(0, idx).cpu().numpy()
-    w_rows = np.arange(rows.shape[0])
-    # reuse the checker on the sampled rows
-    c_ref, k_ref = oracle.assemble_rows(w.pool, gather[rows], delta[rows], oracle.rope_inv_freq(w.theta))
-    assert np.array_equal(ob[:, :512], w.pool[gather[rows], :512])
-    same = delta[rows] == 0
-    assert np.array_equal(ob[same, 512:], w.pool[gather[rows][same], 512:])
-    assert rel_l2(krs.astype(np.float64), k_ref) <= KR_TOL
-    got = oracle.bf16_to_f64(ob[:, 512:])
-    assert np.all(np.abs(got - k_ref) <= _bf16_ulp(k_ref) * 1.0000001)
-    assert w_rows.shape[0] == rows.shape[0]
+    base = t.seq_base()
+    inv = oracle.rope_inv_freq(w.theta)
+    num = den = 0.0
+    rotated = 0
+    for s, (g, d, _) in enumerate(exp):
+        lo, hi = int(base[s]), int(base[s + 1])
+        ob = irm.from_device_bf16(out[lo:hi])
+        krs = kr[lo:hi].cpu().numpy().astype(np.float64)
+        _, k_ref = oracle.assemble_rows(w.pool, g, d, inv)
+        assert np.array_equal(ob[:, :512], w.pool[g, :512]), s
+        same = d == 0
+        assert np.array_equal(ob[same, 512:], w.pool[g[same], 512:]), s
+        assert np.array_equal(krs[same], k_ref[same]), s
+        assert rel_l2(krs, k_ref) <= KR_TOL, s
+        got = oracle.bf16_to_f64(ob[:, 512:])
+        assert np.all(np.abs(got - k_ref) <= _kr_bound(k_ref, w.pool[g, 512:])), s
+        num += float(np.sum((krs - k_ref) ** 2))
+        den += float(np.sum(k_ref ** 2))
+        rotated += int(np.count_nonzero(~same))
+    assert np.sqrt(num / den) <= KR_TOL
+    assert rotated > 0 and base[-1] == gather.shape[0]
+
+
+def test_rotate_gather_full_size():
+    """64 requests x 32768 tokens over a 4096-chunk registry with chunk
+    lengths uniform in [32, 512] (the benchmarked launch), every row."""
+    _check_gather_every_row(rotate_gather_batch())
+
+
+def test_rotate_gather_cdc_lengths_full_size():
+    """The same batch shape with CDC-like chunk lengths (32 plus a geometric
+    tail, mean about 127, clamped at 512): about twice the entries per
+    request, so more entry boundaries inside every 8-row slice."""
+    w = rotate_gather_cdc_batch()
+    lens = w.chunks["len"].astype(np.float64)
+    assert 100 < lens.mean() < 160 and lens.min() >= 1 and lens.max() <= 512
+    _check_gather_every_row(w)
 
 
 # ---------------------------------------------------------------- GQA/MHA comparison path
@@ -382,26 +421,44 @@ def test_decode_fused_equals_gather_then_decode(heads, tiny):
     assert np.array_equal(fused[1], plain[1])
 
 
-def test_decode_batched_full_size_sampled():
-    """Batch 64 x 8192 tokens, 16 heads (benchmarked launch: default splits)."""
+def test_decode_batched_full_size():
+    """Batch 64 x 8192 tokens, 16 heads (benchmarked launch: default splits),
+    every sequence and head against the oracle; a second call gives the same
+    bits."""
     w = batched_decode()
-    o, l = _gpu_decode(w, w.n_splits)
-    seqs = [0, 17, 63]
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    o, l = _gpu_decode(w, w.n_splits, table=t, pool=pool)
+    o2, l2 = _gpu_decode(w, w.n_splits, table=t, pool=pool)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    assert rel_l2(o, o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l - l_ref)) <= LSE_TOL
+    for b in range(w.n_seq):
+        assert rel_l2(o[b], o_ref[b]) <= ATTN_TOL, b
+
+
+def test_decode_long_full_size():
+    """Batch 32 x 32768 tokens, 128 heads, 16 splits (benchmarked launch):
+    eight sequences spread over the batch (so over several XCDs and split
+    runs), every head of both 64-head blocks, against the oracle; every
+    output finite; a second call gives the same bits."""
+    w = long_decode()
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    o, l = _gpu_decode(w, w.n_splits, table=t, pool=pool)
+    o2, l2 = _gpu_decode(w, w.n_splits, table=t, pool=pool)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    seqs = [0, 5, 9, 14, 18, 23, 27, 31]
     o_ref, l_ref = _oracle_decode(w, seqs)
     assert rel_l2(o[seqs], o_ref) <= ATTN_TOL
     assert np.max(np.abs(l[seqs] - l_ref)) <= LSE_TOL
+    for i, b in enumerate(seqs):
+        assert rel_l2(o[b], o_ref[i]) <= ATTN_TOL, b
+        for blk in (0, 1):
+            hs = slice(64 * blk, 64 * blk + 64)
+            assert rel_l2(o[b, hs], o_ref[i, hs]) <= ATTN_TOL, (b, blk)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
-
-
-def test_decode_long_full_size_sampled():
-    """Batch 32 x 32768 tokens, 128 heads, 16 splits (benchmarked launch)."""
-    w = long_decode()
-    o, l = _gpu_decode(w, w.n_splits)
-    seqs, heads = [0, 31], [0, 1, 63, 64, 127]
-    o_ref, l_ref = _oracle_decode(w, seqs, heads)
-    assert rel_l2(o[seqs][:, heads], o_ref) <= ATTN_TOL
-    assert np.max(np.abs(l[seqs][:, heads] - l_ref)) <= LSE_TOL
-    assert np.all(np.isfinite(o))
 
 
 # ---------------------------------------------------------------- prefill
@@ -465,23 +522,50 @@ def test_prefill_assembled_equals_fused(seed, heads, N, nq):
     assert np.max(np.abs(asm[1].cpu().numpy().astype(np.float64) - l_ref)) <= LSE_TOL
 
 
-def test_prefill_assembled_full_size_sampled():
+# Queries of the full-size tail-prefill compared with the oracle: both ends,
+# and all four queries of workgroup blocks spread over the 1024 blocks of
+# four (so every scoring wave's position in a block is covered).
+_FULL_QIDS = sorted({q for k in (0, 1, 2, 3, 255, 256, 511, 512, 513, 700, 767, 900, 1000, 1021, 1022, 1023)
+                     for q in range(4 * k, 4 * k + 4)} | {2047, 2048, 3001})
+
+
+_FULL_PREFILL_REF = {}
+
+
+def _full_prefill_oracle(w):
+    """Oracle outputs of the full-size tail-prefill at _FULL_QIDS (computed
+    once per test session: two tests share them)."""
+    if "ref" not in _FULL_PREFILL_REF:
+        _FULL_PREFILL_REF["ref"] = _oracle_prefill(w, _FULL_QIDS)
+    return _FULL_PREFILL_REF["ref"]
+
+
+def _check_full_prefill(w, o, l):
+    qids = _FULL_QIDS
+    o_ref, l_ref = _full_prefill_oracle(w)
+    assert len(qids) >= 64
+    assert rel_l2(o[qids], o_ref) <= ATTN_TOL
+    assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
+    for i, q in enumerate(qids):
+        assert rel_l2(o[q], o_ref[i]) <= ATTN_TOL, q
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+def test_prefill_assembled_full_size():
     """The benchmarked pair: rotate-gather of the 65536-row cache, then 4096
-    queries over it."""
+    queries over it; two calls give the same bits."""
     w = tail_prefill()
     pool = irm.to_device_bf16(w.pool)
     t = _table(w)
     ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
     kv = irm.rotate_gather(t, pool)
     out, lse = irm.mla_prefill_assembled(ql, qr, w.q_pos0, kv, scale=w.scale, want_lse=True)
+    out2, lse2 = irm.mla_prefill_assembled(ql, qr, w.q_pos0, kv, scale=w.scale, want_lse=True)
     _sync()
-    o = oracle.bf16_to_f64(irm.from_device_bf16(out))
-    l = lse.cpu().numpy().astype(np.float64)
-    qids = [0, 1, 2046, 4094, 4095]
-    o_ref, l_ref = _oracle_prefill(w, qids)
-    assert rel_l2(o[qids], o_ref) <= ATTN_TOL
-    assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
-    assert np.all(np.isfinite(o))
+    o_bits = irm.from_device_bf16(out)
+    assert np.array_equal(o_bits, irm.from_device_bf16(out2))
+    assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+    _check_full_prefill(w, oracle.bf16_to_f64(o_bits), lse.cpu().numpy().astype(np.float64))
 
 
 def test_prefill_last_query_equals_decode():
@@ -495,15 +579,20 @@ def test_prefill_last_query_equals_decode():
     assert np.max(np.abs(l[-1] - ld[0])) <= LSE_TOL
 
 
-def test_prefill_full_size_sampled():
-    """4096 queries at positions 61440.. over a 65536-row assembled cache."""
+def test_prefill_full_size():
+    """4096 queries at positions 61440.. over the 65536-row table with
+    rotation on load (one kernel); two calls give the same bits."""
     w = tail_prefill()
-    o, l = _gpu_prefill(w)
-    qids = [0, 1, 2047, 4094, 4095]
-    o_ref, l_ref = _oracle_prefill(w, qids)
-    assert rel_l2(o[qids], o_ref) <= ATTN_TOL
-    assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
-    assert np.all(np.isfinite(o))
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    ql, qr = irm.to_device_bf16(w.q_lat), irm.to_device_bf16(w.q_rope)
+    out, lse = irm.mla_prefill_tail(ql, qr, w.q_pos0, t, pool, scale=w.scale, want_lse=True)
+    out2, lse2 = irm.mla_prefill_tail(ql, qr, w.q_pos0, t, pool, scale=w.scale, want_lse=True)
+    _sync()
+    o_bits = irm.from_device_bf16(out)
+    assert np.array_equal(o_bits, irm.from_device_bf16(out2))
+    assert np.array_equal(lse.cpu().numpy(), lse2.cpu().numpy())
+    _check_full_prefill(w, oracle.bf16_to_f64(o_bits), lse.cpu().numpy().astype(np.float64))
 
 
 # ---------------------------------------------------------------- non-absorbed prefill
