@@ -241,6 +241,29 @@ irm_status irm_mla_decode(const void* q_latent, const void* q_rope, const irm_ta
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * irm_mla_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments and results as irm_mla_decode, without the
+ * workspace arguments.  The split pass keeps its partial states in a device
+ * array the library holds for each GPU until the process ends (64 MiB; its
+ * device address is looked up on the first call on that GPU).  The call
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library call.
+ *   Limit: n_seq * parts * n_heads * (512 + 2) * 4 bytes (each half rounded
+ *   up to 256) must fit in 64 MiB, where parts is the number of partial
+ *   states the split pass writes per sequence (n_splits, or fewer when one
+ *   workgroup streams a run of splits); else EWORKSPACE, before any launch.
+ *   The batched 64 x 8192 x 16-head and the 32 x 32768 x 128-head decodes fit.
+ * Every call on a GPU shares that GPU's array: calls that may overlap on one
+ * GPU (different streams without ordering between them) race and give wrong
+ * results; order them on one stream.  No state carries over between calls
+ * (every partial slot is written before it is read), so nothing needs
+ * clearing.
+ */
+irm_status irm_mla_decode_noalloc(const void* q_latent, const void* q_rope, const irm_table* t,
+                                  const void* pool, uint64_t pool_rows, uint32_t n_heads,
+                                  uint32_t n_splits, float scale, void* out, float* lse, void* stream);
+
+/*
  * Chunked tail-prefill for one sequence (the table must hold exactly one
  * sequence of N rows): n_q query tokens at positions q_pos0 .. q_pos0+n_q-1
  * attend causally (row t visible to query i iff t <= q_pos0 + i) over the

@@ -36,7 +36,7 @@ EXPORTS = (
     "irm_table_info", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
     "irm_table_set_rope", "irm_table_prepare",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
-    "irm_mla_decode", "irm_mla_prefill_tail", "irm_mla_prefill_assembled", "irm_gqa_workspace",
+    "irm_mla_decode", "irm_mla_decode_noalloc", "irm_mla_prefill_tail", "irm_mla_prefill_assembled", "irm_gqa_workspace",
     "irm_gqa_rotate_gather", "irm_mla_kv_upproj", "irm_mla_prefill_nonabsorbed",
     "irm_cdc_params_default", "irm_cdc_split", "irm_xxh64", "irm_registry_create",
     "irm_registry_destroy", "irm_registry_info", "irm_registry_assemble",
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "irm_rotate_gather": (ctypes.c_int, [vp, vp, u64, vp, vp, vp]),
         "irm_mla_decode_workspace": (ctypes.c_int, [vp, u32, u32, P(sz)]),
         "irm_mla_decode": (ctypes.c_int, [vp, vp, vp, vp, u64, u32, u32, ctypes.c_float, vp, vp, vp, sz, vp]),
+        "irm_mla_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, u64, u32, u32, ctypes.c_float, vp, vp, vp]),
         "irm_mla_prefill_tail": (ctypes.c_int, [vp, vp, i32, u32, vp, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
         "irm_mla_prefill_assembled": (ctypes.c_int, [vp, vp, i32, u32, vp, u64, u32, ctypes.c_float, vp, vp, vp]),
         "irm_gqa_workspace": (ctypes.c_int, [vp, u32, P(sz)]),
@@ -318,6 +319,28 @@ def mla_decode(q_lat, q_rope, table: Table, pool, n_splits: int = 0, scale: floa
                                 n_splits, float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "irm_mla_decode")
     return (out, lse) if want_lse else out
+
+
+def mla_decode_noalloc(q_lat, q_rope, table: Table, pool, out, lse=None, n_splits: int = 0,
+                       scale: float = DEFAULT_SCALE, stream=None):
+    """mla_decode without any device allocation: the caller passes out (bf16
+    [B][H][512]) and optionally lse (float [B][H]); the library keeps the
+    split partials in its own per-GPU scratch array (calls that overlap on
+    one GPU race; order them on one stream)."""
+    import torch
+    _bf16_2d(pool, ROW, "pool")
+    _bf16_2d(q_lat, D_LATENT, "q_lat")
+    _bf16_2d(q_rope, D_ROPE, "q_rope")
+    B, H = q_lat.shape[0], q_lat.shape[1]
+    if B != table.n_seq or tuple(q_rope.shape) != (B, H, D_ROPE):
+        raise ValueError("q_lat/q_rope must be [n_seq][H][512] / [n_seq][H][64]")
+    check_out(out, (B, H, D_LATENT), pool.device)
+    if lse is not None:
+        check_out(lse, (B, H), pool.device, "lse", torch.float32)
+    _check(lib().irm_mla_decode_noalloc(_ptr(q_lat), _ptr(q_rope), table.handle, _ptr(pool), pool.shape[0], H,
+                                        n_splits, float(scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "irm_mla_decode_noalloc")
+    return (out, lse) if lse is not None else out
 
 
 def mla_prefill_tail(q_lat, q_rope, q_pos0: int, table: Table, pool, scale: float = DEFAULT_SCALE,

@@ -178,6 +178,38 @@ extern "C" irm_status irm_mla_decode(const void* q_latent, const void* q_rope, c
                             static_cast<hipStream_t>(stream));
 }
 
+extern "C" irm_status irm_mla_decode_noalloc(const void* q_latent, const void* q_rope, const irm_table* t,
+                                             const void* pool, uint64_t pool_rows, uint32_t n_heads,
+                                             uint32_t n_splits, float scale, void* out, float* lse, void* stream) {
+  static const char* fn = "irm_mla_decode_noalloc";
+  irm_status st = need_uploaded(t, fn);
+  if (st != IRM_OK) return st;
+  if ((st = check_heads(n_heads, fn)) != IRM_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(IRM_EINVAL, std::string(fn) + ": scale must be finite and > 0");
+  if (t->n_seq == 0) return IRM_OK;
+  if (t->min_seq_len == 0) return fail(IRM_EINVAL, std::string(fn) + ": every sequence needs at least one row");
+  if ((st = check_pool(t, pool, pool_rows, fn)) != IRM_OK) return st;
+  if (!q_latent || !q_rope || !out || !aligned16(q_latent) || !aligned16(q_rope) || !aligned16(out))
+    return fail(IRM_EINVAL, std::string(fn) + ": q_latent, q_rope and out must be non-NULL and 16-byte aligned");
+  if (n_splits > 4096) return fail(IRM_EUNSUPPORTED, std::string(fn) + ": n_splits above 4096");
+  if ((st = check_device()) != IRM_OK) return st;
+  const uint32_t S = n_splits ? n_splits : irm::decode_default_splits(t, n_heads / 16);
+  // the split pass writes n_parts partial states per (sequence, head)
+  const size_t parts = (size_t)t->n_seq * irm::decode_parts(t, n_heads, S) * n_heads;
+  const size_t acc_bytes = irm::align_up(parts * IRM_D_LATENT * sizeof(float));
+  const size_t need = acc_bytes + irm::align_up(parts * 2 * sizeof(float));
+  if (need > irm::kDecodeScratchBytes)
+    return fail(IRM_EWORKSPACE, std::string(fn) + ": partial states need " + std::to_string(need) +
+                                    " bytes, more than the library's " + std::to_string(irm::kDecodeScratchBytes) +
+                                    "-byte scratch; use irm_mla_decode with a caller workspace");
+  void* ws = nullptr;
+  if ((st = irm::decode_scratch(&ws)) != IRM_OK) return st;
+  float* ws_acc = static_cast<float*>(ws);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + acc_bytes);
+  return irm::launch_decode(t, q_latent, q_rope, pool, pool_rows, n_heads, S, scale, out, lse, ws_acc, ws_ml,
+                            static_cast<hipStream_t>(stream));
+}
+
 extern "C" irm_status irm_mla_prefill_tail(const void* q_latent, const void* q_rope, int32_t q_pos0,
                                            uint32_t n_q, const irm_table* t, const void* pool,
                                            uint64_t pool_rows, uint32_t n_heads, float scale,

@@ -9,8 +9,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "irm_attn.h"
 #include "irm_launch.h"
+
+// Partial states of the split pass for callers that cannot allocate: one
+// array per device, held until the process ends.  Host code never passes
+// `scratch` itself to a kernel (on the host it only names the symbol); it
+// passes the device address decode_scratch() looks up once per device.
+static __device__ __align__(256) unsigned char scratch[irm::kDecodeScratchBytes];
 
 namespace irm {
 namespace {
@@ -413,6 +421,26 @@ irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_ro
   else
     hipLaunchKernelGGL(decode_combine_kernel<0>, cgrid, cblock, 0, s, ws_acc, ws_ml, o16, lse, n_heads, n_parts);
   return launch_check("irm_mla_decode: combine kernel");
+}
+
+irm_status decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  irm_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st != IRM_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(IRM_EUNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    st = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != IRM_OK) return st;
+    if (!p || reinterpret_cast<uintptr_t>(p) % kAlign)
+      return fail(IRM_EHIP, "hipGetSymbolAddress(scratch): no aligned device address");
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return IRM_OK;
 }
 
 }  // namespace irm

@@ -26,6 +26,12 @@ uint32_t decode_default_splits(const irm_table* t, uint32_t n_groups);
 // 64-head kernel merges runs of splits when the device has fewer compute
 // units than (sequence, split, head block) triples).
 uint32_t decode_parts(const irm_table* t, uint32_t n_heads, uint32_t n_splits);
+// The library's own decode workspace for callers that cannot allocate: a
+// device array of kDecodeScratchBytes per device, its address looked up
+// once per device (hipGetSymbolAddress) with that device current.
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+irm_status decode_scratch(void** ptr);
 irm_status launch_decode(const irm_table* t, const void* q_lat, const void* q_rope, const void* pool,
                          uint64_t pool_rows, uint32_t n_heads, uint32_t n_splits, float scale, void* out,
                          float* lse, float* ws_acc, float* ws_ml, hipStream_t s);
