@@ -226,24 +226,35 @@ _SCRUB = []
 
 
 def time_cold(fn, n: int = 5):
-    """Median event time (ms) of fn over n launches, each after a 512 MB
-    write that evicts the 256 MB Infinity Cache (the scrub is outside the
-    events): what the kernel does when none of its inputs sit in a cache."""
+    """Median event time (ms) of single calls of fn, each after a 512 MB
+    write and then a read of the same 512 MB (outside the events), which
+    evicts the 256 MB Infinity Cache: what the kernel does when none of its
+    inputs sit in a cache.  The read after the write drains the write's dirty
+    lines before the timed call (a write alone leaves up to 256 MB of dirty
+    lines whose write-back would be charged to the kernel: +15% on the
+    batched decode).  Returns (cold ms, warm ms of the same single-call
+    method)."""
     import torch
     if not _SCRUB:
-        _SCRUB.append(torch.empty(512 << 20, dtype=torch.uint8, device="cuda"))
+        _SCRUB.append(torch.ones(512 << 18, dtype=torch.int32, device="cuda"))
     scrub = _SCRUB[0]
-    ts = []
-    for k in range(n):
-        scrub.fill_(k & 0xff)
+
+    def one(cold: bool):
+        if cold:
+            scrub.fill_(2)
+            scrub.sum()
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
         b.record()
         torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ts.sort()
-    return ts[len(ts) // 2]
+        return a.elapsed_time(b)
+
+    one(False)
+    cold = sorted(one(True) for _ in range(n))
+    warm = sorted(one(False) for _ in range(n))
+    return cold[n // 2], warm[n // 2]
 
 
 def time_events(fn, n: int = 10):
@@ -287,11 +298,12 @@ def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
     alg_bytes = 2 * ROW_BYTES * tokens
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic("rotate_gather_kernel" + ("" if make is None else ":" + w.name))
-    cold_ms = time_cold(lambda: irm.rotate_gather(t, pool, out=out))
+    cold_ms, warm1_ms = time_cold(lambda: irm.rotate_gather(t, pool, out=out))
     prep_ms = time_events(lambda: t.prepare(inv))
     upload_ms = time_events(lambda: t.upload(inv, dev_buf=t._dev))
-    log(f"{label}: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms (median), {achieved:.0f} GB/s; "
-        f"after a cache scrub {cold_ms:.3f} ms; prepare {prep_ms:.3f} ms, upload with its copy {upload_ms:.3f} ms")
+    log(f"{label}: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms (median), {achieved:.0f} GB/s; single calls: "
+        f"after a cache scrub {cold_ms:.3f} ms, warm {warm1_ms:.3f} ms; prepare {prep_ms:.3f} ms, upload with its "
+        f"copy {upload_ms:.3f} ms")
     res = {
         "tokens": tokens, "ms_per_step": ms, "kernel_ms": kern_ms, "entries": int(t.n_chunks),
         "mean_entry_len": round(tokens / max(1, t.n_chunks), 1),
@@ -306,7 +318,8 @@ def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
                      "kernel_ms_median": round(kern_ms, 4), "kernel_ms_mean": round(kern_mean, 4),
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "cold_cache_kernel_ms": round(cold_ms, 4),
-                     "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "warm_single_call_ms": round(warm1_ms, 4)},
         "sclk": clk,
         "workload": w, "table": t,
     }
@@ -363,7 +376,7 @@ def leg_decode(args, irm, torch, synth, name, make):
             ev[1].record()
 
     ms, kern_ms, kern_mean, clk = time_leg(step, args.steps, args.warmup)
-    cold_ms = time_cold(lambda: step(None))
+    cold_ms, warm1_ms = time_cold(lambda: step(None))
 
     # the price of the rotation on load
     t0 = irm.Table(_delta0_chunks(w.chunks), w.seq_first, w.pool.shape[0]).upload(irm.rope_inv_freq(w.theta))
@@ -393,7 +406,7 @@ def leg_decode(args, irm, torch, synth, name, make):
     flops = 2 * (576 + 512) * H * t.total_rows
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     log(f"{name}: {kern_ms:.3f} ms/call (median), {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s; "
-        f"after a cache scrub {cold_ms:.3f} ms; rotation {rot}")
+        f"single calls: after a cache scrub {cold_ms:.3f} ms, warm {warm1_ms:.3f} ms; rotation {rot}")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"{name}: oracle on a sample of the batch")
@@ -408,7 +421,8 @@ def leg_decode(args, irm, torch, synth, name, make):
                      "kernel_ms_median": round(kern_ms, 4), "kernel_ms_mean": round(kern_mean, 4),
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "cold_cache_kernel_ms": round(cold_ms, 4),
-                     "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "warm_single_call_ms": round(warm1_ms, 4)},
         "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
         "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         "rotation_on_load": rot,

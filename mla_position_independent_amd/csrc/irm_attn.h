@@ -660,7 +660,17 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[j][i] = ((int32_t)(16 * j + 4 * hq + i) > lv) ? -INFINITY : acc[j][i];
+      for (int i = 0; i < 4; ++i) sc[j][i] = acc[j][i];
+    // lv is the same for the whole wave: only the tiles that reach past the
+    // wave's last visible row (the end of a range, a query's own position)
+    // need the mask
+    if (lv < kTileRows - 1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((int32_t)(16 * j + 4 * hq + i) > lv) sc[j][i] = -INFINITY;
+    }
     float p[2][4], alpha;
     const bool moved = softmax_scores(sc, c, m, l, p, alpha);
     sm.pfrag[t & 1][s][lane] = __builtin_bit_cast(uint4, pack_p8(p[0], p[1]));
