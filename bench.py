@@ -226,14 +226,15 @@ _SCRUB = []
 
 
 def time_cold(fn, n: int = 5):
-    """Median event time (ms) of single calls of fn, each after a 512 MB
-    write and then a read of the same 512 MB (outside the events), which
-    evicts the 256 MB Infinity Cache: what the kernel does when none of its
-    inputs sit in a cache.  The read after the write drains the write's dirty
-    lines before the timed call (a write alone leaves up to 256 MB of dirty
-    lines whose write-back would be charged to the kernel: +15% on the
-    batched decode).  Returns (cold ms, warm ms of the same single-call
-    method)."""
+    """Median event time (ms) of fn over n launches, each right behind a 512 MB
+    write and a read of the same 512 MB on the same stream, which evict the
+    256 MB Infinity Cache.  The read after the write drains the write's dirty
+    lines before fn starts (a write alone leaves up to 256 MB of dirty lines
+    whose write-back is charged to fn: +15% on the batched decode), and the
+    scrub is enqueued together with fn, so fn is already queued when the
+    scrub ends and the events hold fn's GPU time alone (no launch gap), to be
+    set beside the timed loop's back-to-back median.  Returns (cold ms, ms
+    of the same calls behind a 32 MB read instead of the scrub)."""
     import torch
     if not _SCRUB:
         _SCRUB.append(torch.ones(512 << 18, dtype=torch.int32, device="cuda"))
@@ -243,7 +244,8 @@ def time_cold(fn, n: int = 5):
         if cold:
             scrub.fill_(2)
             scrub.sum()
-        torch.cuda.synchronize()
+        else:
+            scrub[: 8 << 20].sum()  # a 32 MB read ahead, long enough that fn is queued when it ends
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
@@ -258,19 +260,18 @@ def time_cold(fn, n: int = 5):
 
 
 def time_events(fn, n: int = 10):
-    """Median event time (ms) of fn over n back-to-back calls, after one
-    untimed call."""
+    """Median event time (ms) of fn over n back-to-back calls (events around
+    each call, one synchronisation at the end, as in the timed loops), after
+    one untimed call."""
     import torch
     fn()
-    ts = []
-    for _ in range(n):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
         a.record()
         fn()
         b.record()
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    ts.sort()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
     return ts[len(ts) // 2]
 
 
@@ -301,8 +302,8 @@ def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
     cold_ms, warm1_ms = time_cold(lambda: irm.rotate_gather(t, pool, out=out))
     prep_ms = time_events(lambda: t.prepare(inv))
     upload_ms = time_events(lambda: t.upload(inv, dev_buf=t._dev))
-    log(f"{label}: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms (median), {achieved:.0f} GB/s; single calls: "
-        f"after a cache scrub {cold_ms:.3f} ms, warm {warm1_ms:.3f} ms; prepare {prep_ms:.3f} ms, upload with its "
+    log(f"{label}: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms (median), {achieved:.0f} GB/s; behind a cache scrub "
+        f"{cold_ms:.3f} ms, behind a small kernel {warm1_ms:.3f} ms; prepare {prep_ms:.3f} ms, upload with its "
         f"copy {upload_ms:.3f} ms")
     res = {
         "tokens": tokens, "ms_per_step": ms, "kernel_ms": kern_ms, "entries": int(t.n_chunks),
@@ -319,7 +320,7 @@ def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "cold_cache_kernel_ms": round(cold_ms, 4),
                      "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "warm_single_call_ms": round(warm1_ms, 4)},
+                     "warm_behind_small_kernel_ms": round(warm1_ms, 4)},
         "sclk": clk,
         "workload": w, "table": t,
     }
@@ -406,7 +407,7 @@ def leg_decode(args, irm, torch, synth, name, make):
     flops = 2 * (576 + 512) * H * t.total_rows
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     log(f"{name}: {kern_ms:.3f} ms/call (median), {achieved:.0f} GB/s, {flops / kern_ms / 1e9:.0f} TFLOP/s; "
-        f"single calls: after a cache scrub {cold_ms:.3f} ms, warm {warm1_ms:.3f} ms; rotation {rot}")
+        f"behind a cache scrub {cold_ms:.3f} ms, behind a small kernel {warm1_ms:.3f} ms; rotation {rot}")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"{name}: oracle on a sample of the batch")
@@ -422,7 +423,7 @@ def leg_decode(args, irm, torch, synth, name, make):
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "cold_cache_kernel_ms": round(cold_ms, 4),
                      "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "warm_single_call_ms": round(warm1_ms, 4)},
+                     "warm_behind_small_kernel_ms": round(warm1_ms, 4)},
         "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
         "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         "rotation_on_load": rot,
