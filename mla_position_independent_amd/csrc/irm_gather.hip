@@ -62,19 +62,26 @@ __global__ void rowmap_kernel(Image im, uint32_t total_rows, uint4* __restrict__
 // ---------------------------------------------------------------------------
 // rotate-gather: a grid-stride stream over the assembled rows' 16-byte units
 //
-// Unit u is unit u % 72 of assembled row u / 72.  Each thread keeps kUnitsInFlight
-// units in flight per step, 256 apart, so a wave moves 1 KB per load and
-// store instruction; the row's record in the row map (pool row, entry)
-// comes through the cache, shared by the 72 units of a row.  c_KV units are
-// copied; k_r units of rotated rows are turned with the entry's (cos, sin).
-// Few units per thread and many resident waves keep more bytes in flight
-// than one large tile per workgroup (5.72 TB/s against 5.34 TB/s for 18
-// units per thread on 64-row tiles).
+// Unit u is unit u % 72 of assembled row u / 72.  A workgroup is one wave;
+// each lane keeps kUnitsInFlight units in flight per step, 64 apart, so the
+// wave moves 1 KB per load and store instruction and a workgroup 4 KB; the
+// row's record in the row map (pool row, entry) comes through the cache,
+// shared by the 72 units of a row.  c_KV units are copied; k_r units of
+// rotated rows are turned with the entry's (cos, sin).  Measured on the
+// 64 x 32768-token batch: one-wave workgroups of 4 units per lane move
+// 6.0-6.4 TB/s against 5.7 TB/s for four-wave workgroups (2-8 units per
+// lane and 128-lane workgroups measured too), and with them pool loads
+// through the cache beat non-temporal ones by 3-6%, behind a cache scrub as
+// well as back to back; the stores stay non-temporal (plain stores: 5.7
+// TB/s).  Short workgroups keep the chip's requests on a narrow window of
+// addresses, as a plain copy of the same bytes shows (6.7 TB/s with one-wave
+// workgroups, 5.9 TB/s with four-wave ones).
 // ---------------------------------------------------------------------------
 constexpr int kUnitsInFlight = 4;
-constexpr int kGatherStep = kUnitsInFlight * kThreads;  // units per workgroup step
+constexpr int kGatherThreads = 64;
+constexpr int kGatherStep = kUnitsInFlight * kGatherThreads;  // units per workgroup step
 
-__global__ __launch_bounds__(kThreads) void rotate_gather_kernel(Image im, uint64_t n_units,
+__global__ __launch_bounds__(kGatherThreads) void rotate_gather_kernel(Image im, uint64_t n_units,
                                                                   const uint4* __restrict__ pool,
                                                                   uint4* __restrict__ out,
                                                                   float* __restrict__ kr_f32) {
@@ -87,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void rotate_gather_kernel(Image im, uint6
     uint4 rec[kUnitsInFlight];
 #pragma unroll
     for (int k = 0; k < kUnitsInFlight; ++k) {
-      const uint64_t u = min(base + (uint64_t)k * kThreads + threadIdx.x, n_units - 1);
+      const uint64_t u = min(base + (uint64_t)k * kGatherThreads + threadIdx.x, n_units - 1);
       row[k] = u / kUnitsPerRow;
       col[k] = (uint32_t)(u - row[k] * kUnitsPerRow);
       rec[k] = im.rowmap[row[k]];
@@ -95,10 +102,10 @@ __global__ __launch_bounds__(kThreads) void rotate_gather_kernel(Image im, uint6
     u32x4_t v[kUnitsInFlight];
 #pragma unroll
     for (int k = 0; k < kUnitsInFlight; ++k)
-      v[k] = __builtin_nontemporal_load(P + (size_t)rec[k].x * kUnitsPerRow + col[k]);
+      v[k] = P[(size_t)rec[k].x * kUnitsPerRow + col[k]];
 #pragma unroll
     for (int k = 0; k < kUnitsInFlight; ++k) {
-      const uint64_t u = base + (uint64_t)k * kThreads + threadIdx.x;
+      const uint64_t u = base + (uint64_t)k * kGatherThreads + threadIdx.x;
       if (u >= n_units) continue;
       u32x4_t w = v[k];
       if (col[k] >= (uint32_t)kLatUnits) {
@@ -158,7 +165,7 @@ irm_status launch_rotate_gather(const irm_table* t, const void* pool, void* out_
   // one step per workgroup (measured faster than a persistent grid); the
   // grid-stride loop only covers grids past the launch limit
   const uint32_t grid = (uint32_t)(steps < 0x7fffffffull ? steps : 0x7fffffffull);
-  hipLaunchKernelGGL(rotate_gather_kernel, dim3(grid), dim3(kThreads), 0, s, image_of(t), n_units,
+  hipLaunchKernelGGL(rotate_gather_kernel, dim3(grid), dim3(kGatherThreads), 0, s, image_of(t), n_units,
                      static_cast<const uint4*>(pool), static_cast<uint4*>(out_kv), kr_f32);
   return launch_check("rotate-gather kernel");
 }

@@ -40,8 +40,14 @@ __global__ void gqa_trig_kernel(const DevEntry* __restrict__ ents, uint32_t n_en
 // bytes: the two halves of 8 rotation pairs), then the V units (16 bytes).
 // Pair units of rows with a nonzero delta are turned in float with the
 // entry's (cos, sin) and rounded to bf16 (RNE); everything else is copied.
-constexpr int kItemsInFlight = 4;
-constexpr int kGqaStep = kItemsInFlight * kThreads;
+// A workgroup is one wave with one item per lane, pool loads through the
+// cache and non-temporal stores: on the 64 x 32768-token batch over an
+// 8 x 128 pool this moves 6.4 TB/s, against 5.4 TB/s for four-wave
+// workgroups of four items per lane with non-temporal loads (2-4 items per
+// lane and 128-256-lane workgroups measured between the two).
+constexpr int kItemsInFlight = 1;
+constexpr int kGqaThreads = 64;
+constexpr int kGqaStep = kItemsInFlight * kGqaThreads;
 
 struct GqaShape {
   uint32_t half_units;  // units in half a head (head_dim / 16)
@@ -66,7 +72,7 @@ __device__ __forceinline__ u32x4_t turn(const u32x4_t& a, const u32x4_t& b, cons
   return r;
 }
 
-__global__ __launch_bounds__(kThreads) void gqa_rotate_gather_kernel(const uint4* __restrict__ rowmap,
+__global__ __launch_bounds__(kGqaThreads) void gqa_rotate_gather_kernel(const uint4* __restrict__ rowmap,
                                                                       uint64_t n_items, GqaShape g,
                                                                       const float2* __restrict__ trig,
                                                                       const uint4* __restrict__ pool,
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_gather_kernel(const uint4
     uint4 rec[kItemsInFlight];
 #pragma unroll
     for (int k = 0; k < kItemsInFlight; ++k) {
-      const uint64_t it = min(base + (uint64_t)k * kThreads + threadIdx.x, n_items - 1);
+      const uint64_t it = min(base + (uint64_t)k * kGqaThreads + threadIdx.x, n_items - 1);
       row[k] = __umul64hi(it, g.recip);
       col[k] = (uint32_t)(it - row[k] * g.items);
       rec[k] = rowmap[row[k]];
@@ -98,12 +104,12 @@ __global__ __launch_bounds__(kThreads) void gqa_rotate_gather_kernel(const uint4
         u1[k] = u0[k];
       }
       const u32x4_t* src = P + (size_t)rec[k].x * g.row_units;
-      a[k] = __builtin_nontemporal_load(src + u0[k]);
-      b[k] = col[k] < g.n_pairs ? __builtin_nontemporal_load(src + u1[k]) : a[k];
+      a[k] = src[u0[k]];
+      b[k] = col[k] < g.n_pairs ? src[u1[k]] : a[k];
     }
 #pragma unroll
     for (int k = 0; k < kItemsInFlight; ++k) {
-      const uint64_t it = base + (uint64_t)k * kThreads + threadIdx.x;
+      const uint64_t it = base + (uint64_t)k * kGqaThreads + threadIdx.x;
       if (it >= n_items) continue;
       u32x4_t* dst = O + (size_t)row[k] * g.row_units;
       if (col[k] < g.n_pairs) {
@@ -154,7 +160,7 @@ irm_status launch_gqa_rotate_gather(const irm_table* t, const void* pool, uint32
   const uint64_t n_items = t->total_rows * g.items;
   const uint64_t steps = (n_items + kGqaStep - 1) / kGqaStep;
   const uint32_t grid = (uint32_t)(steps < 0x7fffffffull ? steps : 0x7fffffffull);
-  hipLaunchKernelGGL(gqa_rotate_gather_kernel, dim3(grid), dim3(kThreads), 0, s, im.rowmap, n_items, g, trig,
+  hipLaunchKernelGGL(gqa_rotate_gather_kernel, dim3(grid), dim3(kGqaThreads), 0, s, im.rowmap, n_items, g, trig,
                      static_cast<const uint4*>(pool), static_cast<uint4*>(out));
   return launch_check("GQA rotate-gather kernel");
 }
