@@ -55,6 +55,18 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m0));
 }
 
+// The same copy from base + off, base the same for every lane (scalar
+// registers, so its 64-bit address math is scalar) and off a 32-bit per-lane
+// offset: the form for copies of one row, whose source is wave-uniform.
+template <bool kStream = false>
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  if constexpr (kStream)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(m0));
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(m0));
+}
+
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t kr_pos(uint32_t r, uint32_t u) {
@@ -283,7 +295,12 @@ struct WaveSlots {
 template <int R>
 __device__ __forceinline__ void slice_issue_rowmap(const StreamArgs& ra, uint32_t g0, uint4* rm) {
   const uint32_t l = threadIdx.x & 63;
-  if (l < (uint32_t)R) dma16(ra.rowmap + g0 + l, lds_addr(rm));
+  if (l < (uint32_t)R) dma16s(ra.rowmap + (uint32_t)__builtin_amdgcn_readfirstlane(g0), 16 * l, lds_addr(rm));
+}
+
+// Start of pool row src (wave-uniform) as a scalar address.
+__device__ __forceinline__ const unsigned char* pool_row(const StreamArgs& ra, uint32_t src) {
+  return ra.pool + (size_t)(uint32_t)__builtin_amdgcn_readfirstlane(src) * kRowBytes;
 }
 
 // Data of the slice described by rec into tile rows row0.. of the stage with
@@ -303,7 +320,7 @@ __device__ __forceinline__ void slice_issue_data(const StreamArgs& ra, const uin
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const uint32_t r = row0 + k;
-    dma16<true>(ra.pool + (size_t)src[k] * kRowBytes + ((l ^ (r & 15)) << 4), lds_addr(ckv + r * kCkvBytes));
+    dma16s<true>(pool_row(ra, src[k]), (l ^ (r & 15)) << 4, lds_addr(ckv + r * kCkvBytes));
   }
 #pragma unroll
   for (int h = 0; h < R / 8; ++h) {
@@ -515,7 +532,7 @@ __device__ __forceinline__ SliceCopies prep_copies(const StreamArgs& ra, const u
 __device__ __forceinline__ void copy_ckv(const StreamArgs& ra, const SliceCopies& cp, int k, unsigned char* ckv,
                                          uint32_t row0) {
   const uint32_t l = threadIdx.x & 63, r = row0 + k;
-  dma16(ra.pool + (size_t)cp.src[k] * kRowBytes + ((l ^ (r & 15)) << 4), lds_addr(ckv + r * kCkvBytes));
+  dma16s(pool_row(ra, cp.src[k]), (l ^ (r & 15)) << 4, lds_addr(ckv + r * kCkvBytes));
 }
 
 // k_r of the slice's 8 rows into the stage's k_r region (1 KB, one copy).
@@ -649,7 +666,7 @@ __device__ __forceinline__ void score_stream(const StreamArgs& ra, SplitSmem& sm
       if (kk + kAhead < 18) read(kk + kAhead, ring[(kk + kAhead) % (kAhead + 1)]);
       if (kk >= 2 && kk - 2 < kScoreRows) {
         const uint32_t k = kk - 2, r = row0 + k;
-        dma16(ra.pool + (size_t)src[k] * kRowBytes + ((lane ^ (r & 15)) << 4), lds_addr(nx + r * kCkvBytes));
+        dma16s(pool_row(ra, src[k]), (lane ^ (r & 15)) << 4, lds_addr(nx + r * kCkvBytes));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j)

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_private_kernel(DecodeArgs 
   uint32_t r0, r1;
   split_rows(a.seq_base[b + 1] - base, a.n_splits, sp, r0, r1);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hq = lane >> 4, hr = lane & 15;
   const uint32_t head = g * 16 + hr;
 
