@@ -10,11 +10,12 @@
 //  * upproj_kernel: kvh[h][t] = [W_UK[h] c_KV[t] | W_UV[h] c_KV[t]] (bf16,
 //    256 per row and head), a [rows x 512] by [512 x 256] product per head on
 //    v_mfma_f32_16x16x32_bf16, both operands staged through LDS.
-//  * mha_prefill_kernel: causal attention of 128 queries of one head per
-//    workgroup over the head's rows, streamed in 64-row tiles through two
-//    LDS stages with one barrier per tile (two workgroups per compute unit;
-//    64-row tiles measured 12% faster than 32-row tiles in three or four
-//    stages).
+//  * mha_prefill_kernel: causal attention of 256 queries of one head per
+//    workgroup of eight waves over the head's rows, streamed in 64-row tiles
+//    through two LDS stages with one barrier per tile (one workgroup per
+//    compute unit: each tile copied into LDS serves eight waves, measured 8%
+//    faster than two four-wave workgroups of 128 queries; 64-row tiles
+//    measured 12% faster than 32-row tiles in three or four stages).
 
 #include <hip/hip_runtime.h>
 
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void upproj_kernel(UpArgs a) {
 // ---------------------------------------------------------------------------
 // per-head causal prefill
 //
-// Workgroup = (head h, 128 queries); wave w owns queries 32w .. 32w+31 as two
+// Workgroup = (head h, 32 W queries); wave w owns queries 32w .. 32w+31 as two
 // 16-query blocks and walks every tile of the keys they can see.  Scores are
 // S^T = K Q^T (lane (q, r): keys 4q..4q+3 of a 16-key block for query r), so
 // each lane holds 4 scores per key block and query block, and the maximum
@@ -149,20 +150,20 @@ __global__ __launch_bounds__(kThreads) void upproj_kernel(UpArgs a) {
 //
 // Stage of T keys: k_nope [T][256 B] (unit c of row r at c ^ (r & 15)),
 // k_r [T][128 B] (pos128), v [T][256 B] (as k_nope).  Wave w copies rows
-// wT/4 .. (w+1)T/4 - 1 of each part with 1 KB LDS-DMA copies.  With S
+// wT/W .. (w+1)T/W - 1 of each part with 1 KB LDS-DMA copies.  With S
 // stages, tiles t+1 .. t+S-1 are in flight while tile t is computed, and one
 // barrier per tile both publishes tile t and frees the stage of tile t-1.
 // ---------------------------------------------------------------------------
-constexpr int kMhaQ = 128;  // queries per workgroup
-
-template <int T>
+template <int T, int W>
 struct MhaTile {
   static constexpr int kKn = T * 256;
   static constexpr int kKr = T * 128;
   static constexpr int kBytes = 2 * kKn + kKr;
-  static constexpr int kRows = T / 4;                        // rows per wave
+  static constexpr int kRows = T / W;                          // rows per wave
   static constexpr int kCopies = 2 * (kRows / 4) + kRows / 8;  // 1 KB copies per wave
   static constexpr int kBlocks = T / 16;                       // 16-key blocks
+  static constexpr int kQ = 32 * W;                            // queries per workgroup
+  static_assert(kRows % 8 == 0, "whole k_r copies per wave");
 };
 
 struct MhaArgs {
@@ -177,9 +178,9 @@ struct MhaArgs {
   float c;                      // scale * log2(e)
 };
 
-template <int T>
+template <int T, int W>
 __device__ __forceinline__ void mha_issue(const MhaArgs& a, unsigned char* st, uint32_t h, uint32_t t0) {
-  using Tl = MhaTile<T>;
+  using Tl = MhaTile<T, W>;
   const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const unsigned char* head = a.kvh + (size_t)h * a.rows * 512;
   const uint32_t rw = w * Tl::kRows;
@@ -243,9 +244,10 @@ __device__ __forceinline__ bool softmax_blocks(const float (&s)[NB][4], float c,
   return __any(mv);
 }
 
-template <int T, int S>
-__global__ __launch_bounds__(kThreads, 2) void mha_prefill_kernel(MhaArgs a) {
-  using Tl = MhaTile<T>;
+template <int T, int S, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void mha_prefill_kernel(MhaArgs a) {
+  using Tl = MhaTile<T, W>;
+  constexpr uint32_t kMhaQ = Tl::kQ;
   constexpr int NB = Tl::kBlocks;
   __shared__ unsigned char smem[S][Tl::kBytes];
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void mha_prefill_kernel(MhaArgs a) {
 
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
-    if ((uint32_t)i < n_tiles) mha_issue<T>(a, smem[i], h, i * T);
+    if ((uint32_t)i < n_tiles) mha_issue<T, W>(a, smem[i], h, i * T);
   for (uint32_t t = 0; t < n_tiles; ++t) {
     // copies of tiles t+1 .. t+S-2 may stay in flight
     const uint32_t ahead = min(n_tiles - 1 - t, (uint32_t)(S - 2));
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void mha_prefill_kernel(MhaArgs a) {
     else
       wait_dma_all();
     __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
-    if (t + S - 1 < n_tiles) mha_issue<T>(a, smem[(t + S - 1) % S], h, (t + S - 1) * T);
+    if (t + S - 1 < n_tiles) mha_issue<T, W>(a, smem[(t + S - 1) % S], h, (t + S - 1) * T);
     const unsigned char* st = smem[t % S];
     const unsigned char* kn = st;
     const unsigned char* kr = st + Tl::kKn;
@@ -389,7 +391,9 @@ __global__ __launch_bounds__(kThreads, 2) void mha_prefill_kernel(MhaArgs a) {
 // tile shape of the launch: keys per tile, LDS stages
 constexpr int kMhaT = 64;
 constexpr int kMhaS = 2;
-static_assert(kMhaS * MhaTile<kMhaT>::kBytes * 2 <= 160 * 1024, "two workgroups per compute unit");
+constexpr int kMhaW = 8;
+using MhaLaunch = MhaTile<kMhaT, kMhaW>;
+static_assert(kMhaS * MhaLaunch::kBytes * (8 / kMhaW) <= 160 * 1024, "the workgroups of a compute unit fit the LDS");
 static_assert(kMhaS >= 2 && kMhaS <= 4, "stage count");
 
 }  // namespace
@@ -422,10 +426,10 @@ irm_status launch_prefill_nonabsorbed(const void* q_nope, const void* q_rope, in
   a.rows = (uint32_t)kv_rows;
   a.n_heads = n_heads;
   a.n_q = n_q;
-  a.q_blocks = (n_q + kMhaQ - 1) / kMhaQ;
+  a.q_blocks = (n_q + MhaLaunch::kQ - 1) / MhaLaunch::kQ;
   a.q_pos0 = q_pos0;
   a.c = scale * kLog2e;
-  hipLaunchKernelGGL((mha_prefill_kernel<kMhaT, kMhaS>), dim3(a.q_blocks * n_heads), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((mha_prefill_kernel<kMhaT, kMhaS, kMhaW>), dim3(a.q_blocks * n_heads), dim3(64 * kMhaW), 0, s, a);
   return launch_check("non-absorbed prefill kernel");
 }
 
