@@ -269,6 +269,22 @@ def test_decode_workspace_of_an_empty_batch():
     assert res.stdout.strip() == "ok"
 
 
+def test_default_split_count_keeps_64_rows_per_split():
+    # the library's split count when n_splits == 0: enough (sequence, split)
+    # workgroups for the 256 CUs, each split at least 64 rows long; the
+    # workspace of the default equals the workspace of that explicit count
+    def default_splits(t, heads):
+        ws = irm.decode_workspace_bytes(t, heads, 0)
+        return [s for s in range(1, 65) if irm.decode_workspace_bytes(t, heads, s) == ws]
+
+    w = tiny_decode()  # 1 sequence of 1024 rows: 16 splits of 64 rows
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0])
+    assert default_splits(t, 16) == [16]
+    w = batched_decode()  # 64 sequences of 8192 rows: 4 splits fill 256 CUs
+    t = irm.Table(w.chunks, w.seq_first, w.pool.shape[0])
+    assert default_splits(t, 16) == [4]
+
+
 def test_check_out_refuses_outputs_the_kernels_could_overrun():
     import torch
     good = torch.empty((3, 4), dtype=torch.bfloat16)
