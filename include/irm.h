@@ -169,8 +169,9 @@ irm_status irm_table_upload(irm_table* t, const double* inv_freq, void* dev_buf,
 /*
  * The device passes of irm_table_upload without its host-to-device copy: on
  * `stream`, rebuild the row map (one record per assembled row: pool row,
- * delta, entry) from the entries already in the uploaded device image, then
- * the per-entry cos/sin of delta * inv_freq[i] (as irm_table_set_rope).
+ * delta, entry) from the entries already in the uploaded device image, and
+ * the per-entry cos/sin of delta * inv_freq[i] (as irm_table_set_rope), in
+ * one kernel launch.
  * host inv_freq[32].  Requires an uploaded table (EINVAL otherwise); the
  * result is the same as that of irm_table_upload.  This is the per-batch
  * device work of a table whose image reached HBM by a copy made earlier or

@@ -102,9 +102,8 @@ extern "C" irm_status irm_table_prepare(irm_table* t, const double* inv_freq, vo
   for (int i = 0; i < (int)irm::kPairs; ++i)
     if (!std::isfinite(inv_freq[i])) return fail(IRM_EINVAL, "irm_table_prepare: inv_freq not finite");
   if ((st = check_device()) != IRM_OK) return st;
-  st = irm::launch_rowmap(t, static_cast<hipStream_t>(stream));
-  if (st != IRM_OK) return st;
-  return irm_table_set_rope(t, inv_freq, stream);
+  std::memcpy(t->inv_freq, inv_freq, sizeof(t->inv_freq));
+  return irm::launch_prepare(t, inv_freq, static_cast<hipStream_t>(stream));
 }
 
 extern "C" irm_status irm_table_set_rope(irm_table* t, const double* inv_freq, void* stream) {

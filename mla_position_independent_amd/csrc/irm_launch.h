@@ -13,8 +13,8 @@ irm_status hip_check(hipError_t err, const char* what);
 irm_status launch_check(const char* what);
 
 // irm_gather.hip
-irm_status launch_rowmap(const irm_table* t, hipStream_t s);
 irm_status launch_trig(const irm_table* t, const double* inv_freq, hipStream_t s);
+irm_status launch_prepare(const irm_table* t, const double* inv_freq, hipStream_t s);  // row map + trig, one launch
 irm_status launch_gather_index(const irm_table* t, int64_t* pool_row, int32_t* delta, hipStream_t s);
 irm_status launch_rotate_gather(const irm_table* t, const void* pool, void* out_kv, float* kr_f32,
                                 hipStream_t s);
