@@ -687,7 +687,7 @@ def test_prefill_nonabsorbed_full_size_sampled():
     w = tail_prefill()
     q_nope, wk, wv = _na_case(w, 1005)
     o, l, qn, qr = _gpu_nonabsorbed(w, q_nope, wk, wv)
-    qids = [0, 1, 127, 128, 2047, 4095]
+    qids = [0, 1, 127, 128, 255, 256, 2047, 3839, 3840, 4095]  # both ends of 256-query workgroup blocks
     o_ref, l_ref = _oracle_nonabsorbed(w, qn, qr, wk, wv, qids)
     assert rel_l2(o[qids], o_ref) <= ATTN_TOL
     assert np.max(np.abs(l[qids] - l_ref)) <= LSE_TOL
