@@ -45,8 +45,16 @@ def flags() -> list:
     ]
 
 
+# Sources scheduled with another of the compiler's machine-scheduler
+# strategies: the non-absorbed attention kernel needs 230-250 registers, and
+# the default strategy spills it; iterative-ilp fits it in 250 with no spill.
+SCHED_STRATEGY = {"irm_nonabsorbed.hip": "iterative-ilp"}
+
+
 def source_flags(name: str) -> list:
     extra = ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"] if name in VGPR_FORM else []
+    if name in SCHED_STRATEGY:
+        extra += ["-Xarch_device", f"-mllvm=-amdgpu-sched-strategy={SCHED_STRATEGY[name]}"]
     return flags() + extra
 
 

@@ -181,23 +181,24 @@ struct MhaArgs {
 template <int T, int W>
 __device__ __forceinline__ void mha_issue(const MhaArgs& a, unsigned char* st, uint32_t h, uint32_t t0) {
   using Tl = MhaTile<T, W>;
-  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const unsigned char* head = a.kvh + (size_t)h * a.rows * 512;
+  const uint32_t lane = opaque(threadIdx.x & 63), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // row bases of the tile in scalar registers, 32-bit lane offsets (rows past
+  // the last are clamped to it)
+  const unsigned char* hb = a.kvh + ((size_t)h * a.rows + t0) * 512;
+  const unsigned char* kb = a.kv + (size_t)t0 * kRowBytes + kCkvBytes;
+  const uint32_t last = a.rows - 1 - t0;
   const uint32_t rw = w * Tl::kRows;
 #pragma unroll
   for (int i = 0; i < Tl::kRows / 4; ++i) {
     const uint32_t r = rw + 4 * i + (lane >> 4);
-    const uint32_t u = (lane & 15) ^ (r & 15);
-    const unsigned char* src = head + (size_t)min(t0 + r, a.rows - 1) * 512 + 16 * u;
-    dma16(src, lds_addr(st + (rw + 4 * i) * 256));                          // k_nope
-    dma16(src + 256, lds_addr(st + Tl::kKn + Tl::kKr + (rw + 4 * i) * 256));  // v
+    const uint32_t off = min(r, last) * 512 + 16 * ((lane & 15) ^ (r & 15));
+    dma16s(hb, off, lds_addr(st + (rw + 4 * i) * 256));                          // k_nope
+    dma16s(hb + 256, off, lds_addr(st + Tl::kKn + Tl::kKr + (rw + 4 * i) * 256));  // v
   }
 #pragma unroll
   for (int i = 0; i < Tl::kRows / 8; ++i) {
     const uint32_t r = rw + 8 * i + (lane >> 3);
-    const uint32_t u = (lane & 7) ^ ((r >> 1) & 7);
-    dma16(a.kv + (size_t)min(t0 + r, a.rows - 1) * kRowBytes + kCkvBytes + 16 * u,
-          lds_addr(st + Tl::kKn + (rw + 8 * i) * 128));
+    dma16s(kb, min(r, last) * kRowBytes + 16 * ((lane & 7) ^ ((r >> 1) & 7)), lds_addr(st + Tl::kKn + (rw + 8 * i) * 128));
   }
 }
 
@@ -244,16 +245,112 @@ __device__ __forceinline__ bool softmax_blocks(const float (&s)[NB][4], float c,
   return __any(mv);
 }
 
+// Per-lane LDS offsets within a stage, from a lane id the compiler must
+// treat as fresh (so they are formed where used, not held across the loop):
+// the K reads of score step kk (0-3 k_nope unit (4kk + q) ^ rr of row rr,
+// 4-5 k_r) and the transposing V reads of value block vb (see v_bases).  Key
+// block j adds an immediate.
+template <int T, int W>
+__device__ __forceinline__ void mha_k_offsets(uint32_t (&k)[6]) {
+  using Tl = MhaTile<T, W>;
+  const uint32_t lane = opaque(threadIdx.x & 63), q = lane >> 4, rr = lane & 15;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) k[kk] = rr * 256 + ((((uint32_t)(4 * kk) + q) ^ rr) << 4);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) k[4 + kk] = Tl::kKn + pos128(rr, 4 * kk + q);
+}
+
+template <int T, int W>
+__device__ __forceinline__ void mha_v_offsets(uint32_t (&v)[8]) {
+  using Tl = MhaTile<T, W>;
+  const uint32_t lane = opaque(threadIdx.x & 63), q = lane >> 4, rr = lane & 15;
+  const uint32_t x = 4 * q + (rr >> 2), hh = (rr & 3) >> 1;
+  const uint32_t rowo = Tl::kKn + Tl::kKr + x * 256 + ((hh ^ (x & 1)) << 4) + 8 * (rr & 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = rowo + (((uint32_t)i ^ (x >> 1)) << 5);
+}
+
+// One tile: scores, online softmax (kMask: some key of the tile lies past
+// some query of the wave), value products.
+template <int T, int W, bool kMask>
+__device__ __forceinline__ void mha_tile(const unsigned char* st, const bf16x8_t (&qf)[2][6],
+                                         f32x4_t (&o)[8][2], float (&m)[2], float (&l)[2], uint32_t t0,
+                                         int32_t lim0, float c) {
+  using Tl = MhaTile<T, W>;
+  constexpr int NB = Tl::kBlocks;
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const uint32_t q = (threadIdx.x & 63) >> 4;
+  uint32_t koff[6];
+  mha_k_offsets<T, W>(koff);
+
+  // scores: S^T of key blocks j for query blocks b
+  f32x4_t s[2][NB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 6; ++kk) {
+    const unsigned char* p = st + koff[kk];
+    bf16x8_t kf[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      kf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p + (kk < 4 ? 16 * j * 256 : 16 * j * 128)));
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) s[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[b][kk], s[b][j], 0, 0, 0);
+  }
+
+  // online softmax per query block
+  bf16x8_t pb[2][NB / 2];
+  // key t0 + 16j + 4q + i is past query qw + 16b + r when 16j + i > d + 16b
+  const int32_t d = kMask ? (int32_t)opaque((uint32_t)(lim0 - (int32_t)(t0 + 4 * q))) : 0;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float sv[NB][4], p[NB][4], alpha;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (kMask) {
+          sv[j][i] = 16 * j + i > d + 16 * b ? -INFINITY : s[b][j][i];
+        } else {
+          sv[j][i] = s[b][j][i];
+        }
+      }
+    if (softmax_blocks<NB>(sv, c, m[b], l[b], p, alpha)) {
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb) o[vb][b] *= alpha;
+    }
+#pragma unroll
+    for (int pi = 0; pi < NB / 2; ++pi) pb[b][pi] = pack_p8(p[2 * pi], p[2 * pi + 1]);
+  }
+
+  // O^T += V^T P^T, one 32-deep MFMA per pair of key blocks
+  uint32_t voff[8];
+  mha_v_offsets<T, W>(voff);
+#pragma unroll
+  for (int pi = 0; pi < NB / 2; ++pi)
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) {
+      const unsigned char* base = st + voff[vb] + pi * 32 * 256;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)base);
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 16 * 256));
+      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+      for (int b = 0; b < 2; ++b) o[vb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[b][pi], o[vb][b], 0, 0, 0);
+    }
+}
+
 template <int T, int S, int W>
 __global__ __launch_bounds__(64 * W, 8 / W) void mha_prefill_kernel(MhaArgs a) {
   using Tl = MhaTile<T, W>;
   constexpr uint32_t kMhaQ = Tl::kQ;
-  constexpr int NB = Tl::kBlocks;
   __shared__ unsigned char smem[S][Tl::kBytes];
-  typedef short i16x8_t __attribute__((ext_vector_type(8)));
   const uint32_t h = blockIdx.x % a.n_heads;
   const uint32_t qblk = a.q_blocks - 1 - blockIdx.x / a.n_heads;  // longest blocks first
-  const uint32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t q = lane >> 4, r = lane & 15;
   const uint32_t qw = qblk * kMhaQ + 32 * w;                     // first query of the wave
   const uint32_t q_last = min(qblk * kMhaQ + kMhaQ, a.n_q) - 1;  // last valid query of the workgroup
@@ -285,7 +382,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void mha_prefill_kernel(MhaArgs a) {
     for (int b = 0; b < 2; ++b) o[vb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   // a query at position q_pos0 + i sees keys t <= q_pos0 + i
-  const int32_t lim0 = a.q_pos0 + (int32_t)(qw + r), lim1 = lim0 + 16;
+  const int32_t lim0 = a.q_pos0 + (int32_t)(qw + r);
   const uint32_t first_masked = (uint32_t)a.q_pos0 + qw + 1;  // tiles ending at or below this need no mask
 
 #pragma unroll
@@ -302,70 +399,11 @@ __global__ __launch_bounds__(64 * W, 8 / W) void mha_prefill_kernel(MhaArgs a) {
       wait_dma_all();
     __syncthreads();  // tile t is in LDS; every wave is done with tile t - 1
     if (t + S - 1 < n_tiles) mha_issue<T, W>(a, smem[(t + S - 1) % S], h, (t + S - 1) * T);
-    const unsigned char* st = smem[t % S];
-    const unsigned char* kn = st;
-    const unsigned char* kr = st + Tl::kKn;
-    const unsigned char* v = st + Tl::kKn + Tl::kKr;
-
-    // scores: S^T of key blocks j for query blocks b
-    f32x4_t s[2][NB];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) s[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const uint32_t rr = opaque(r);
-#pragma unroll
-    for (int kk = 0; kk < 6; ++kk) {
-      bf16x8_t kf[NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const uint32_t row = 16 * j + rr;
-        const unsigned char* p = kk < 4 ? kn + row * 256 + (((4 * kk + q) ^ rr) << 4) : kr + pos128(row, 4 * (kk - 4) + q);
-        kf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
-      }
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) s[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j], qf[b][kk], s[b][j], 0, 0, 0);
-    }
-
-    // online softmax per query block; the causal mask only near the diagonal
     const uint32_t t0 = t * T;
-    const bool masked = t0 + T > first_masked;
-    bf16x8_t pb[2][NB / 2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float sv[NB][4], p[NB][4], alpha;
-      const int32_t lim = b ? lim1 : lim0;
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int32_t key = (int32_t)(t0 + 16 * j + 4 * q + i);
-          sv[j][i] = (masked && key > lim) ? -INFINITY : s[b][j][i];
-        }
-      if (softmax_blocks<NB>(sv, a.c, m[b], l[b], p, alpha)) {
-#pragma unroll
-        for (int vb = 0; vb < 8; ++vb) o[vb][b] *= alpha;
-      }
-#pragma unroll
-      for (int pi = 0; pi < NB / 2; ++pi) pb[b][pi] = pack_p8(p[2 * pi], p[2 * pi + 1]);
-    }
-
-    // O^T += V^T P^T, one 32-deep MFMA per pair of key blocks
-    const unsigned char* vb8[8];
-    v_bases(v, vb8);
-#pragma unroll
-    for (int pi = 0; pi < NB / 2; ++pi)
-#pragma unroll
-      for (int vb = 0; vb < 8; ++vb) {
-        const unsigned char* base = vb8[vb] + pi * 32 * 256;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)base);
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 16 * 256));
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-#pragma unroll
-        for (int b = 0; b < 2; ++b) o[vb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[b][pi], o[vb][b], 0, 0, 0);
-      }
+    if (t0 + T > first_masked)
+      mha_tile<T, W, true>(smem[t % S], qf, o, m, l, t0, lim0, a.c);
+    else
+      mha_tile<T, W, false>(smem[t % S], qf, o, m, l, t0, lim0, a.c);
   }
 
   // normalise and store: lane (q, r) holds value dims 16vb + 4q .. +3 of query qw + 16b + r
