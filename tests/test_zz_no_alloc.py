@@ -113,3 +113,38 @@ def test_noalloc_binding_allocates_nothing():
     assert torch.cuda.memory_stats()["allocation.all.allocated"] == before
     ref = irm.mla_decode(ql, qr, t, pool, n_splits=4, scale=w.scale, want_lse=True)
     assert _same((out, lse), ref)
+
+
+def test_noalloc_graph_replay():
+    """Captured in a HIP graph (code under capture is what the entry point is
+    for) and replayed, with eager calls of it between the replays and new
+    query values in the captured buffers, the no-alloc decode matches the
+    workspace decode bit for bit on every replay."""
+    import torch
+    from synth import randn_bf16
+    w = random_table(407, [1500, 900, 2600], heads=16, p_hit=0.7, prefix_frac=0.3)
+    pool, t, ql, qr = _inputs(w)
+    out = torch.empty((w.n_seq, 16, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.n_seq, 16), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # the first call on the device, outside the capture
+        irm.mla_decode_noalloc(ql, qr, t, pool, out, lse=lse, n_splits=4, scale=w.scale)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        irm.mla_decode_noalloc(ql, qr, t, pool, out, lse=lse, n_splits=4, scale=w.scale)
+    rng = np.random.default_rng(408)
+    for rep in range(4):
+        if rep >= 2:
+            ql.copy_(irm.to_device_bf16(randn_bf16(rng, tuple(ql.shape))))
+            qr.copy_(irm.to_device_bf16(randn_bf16(rng, tuple(qr.shape))))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), lse.clone())
+        ref = irm.mla_decode(ql, qr, t, pool, n_splits=4, scale=w.scale, want_lse=True)
+        torch.cuda.synchronize()
+        assert _same(got, ref), rep
+        # an eager call on the same scratch between replays
+        assert _same(_noalloc(ql, qr, t, pool, 16, 4, w.scale), ref), rep
