@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libirm.so")
 
 SOURCES = ["irm_table.cpp", "irm_abi.cpp", "irm_producer.cpp", "irm_gather.hip", "irm_decode.hip", "irm_prefill.hip",
-           "irm_gqa.hip", "irm_nonabsorbed.hip"]
+           "irm_gqa.hip", "irm_nonabsorbed.hip", "irm_upproj.hip"]
 DEPS = SOURCES + ["irm_internal.h", "irm_device.h", "irm_attn.h", "irm_launch.h"]
 
 
