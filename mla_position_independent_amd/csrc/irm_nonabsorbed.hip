@@ -41,7 +41,9 @@ __device__ __forceinline__ uint32_t pos128(uint32_t r, uint32_t u) { return r * 
 // order {4q..4q+3, 16+4q..16+4q+3}.
 //
 // Stage of T keys: k_nope [T][256 B] (unit c of row r at c ^ (r & 15)),
-// k_r [T][128 B] (pos128), v [T][256 B] (as k_nope).  Wave w copies rows
+// k_r [T][128 B] (pos128), v [T][256 B] (unit c of row r at c ^ (2r & 15):
+// the transposing reads of 8 consecutive rows then cover all 64 banks, where
+// k_nope's swizzle left them 2-way conflicted).  Wave w copies rows
 // wT/W .. (w+1)T/W - 1 of each part with 1 KB LDS-DMA copies.  With S
 // stages, tiles t+1 .. t+S-1 are in flight while tile t is computed, and one
 // barrier per tile both publishes tile t and frees the stage of tile t-1.
@@ -83,9 +85,10 @@ __device__ __forceinline__ void mha_issue(const MhaArgs& a, unsigned char* st, u
 #pragma unroll
   for (int i = 0; i < Tl::kRows / 4; ++i) {
     const uint32_t r = rw + 4 * i + (lane >> 4);
-    const uint32_t off = min(r, last) * 512 + 16 * ((lane & 15) ^ (r & 15));
-    dma16s(hb, off, lds_addr(st + (rw + 4 * i) * 256));                          // k_nope
-    dma16s(hb + 256, off, lds_addr(st + Tl::kKn + Tl::kKr + (rw + 4 * i) * 256));  // v
+    const uint32_t rb = min(r, last) * 512;
+    dma16s(hb, rb + 16 * ((lane & 15) ^ (r & 15)), lds_addr(st + (rw + 4 * i) * 256));  // k_nope
+    dma16s(hb + 256, rb + 16 * ((lane & 15) ^ (2 * r & 15)),
+           lds_addr(st + Tl::kKn + Tl::kKr + (rw + 4 * i) * 256));                      // v
   }
 #pragma unroll
   for (int i = 0; i < Tl::kRows / 8; ++i) {
@@ -131,7 +134,8 @@ __device__ __forceinline__ bool softmax_blocks(const float (&s)[NB][4], float c,
 // 4-5 k_r) and the transposing V reads of value block vb (as ct_bases in
 // irm_attn.h, here on 256-byte rows: lane (q, s) reads row x = 4q + s/4, 8
 // bytes of unit 2vb + hh, hh = (s % 4) / 2, which sits at position
-// (2vb + hh) ^ x).  Key block j adds an immediate.
+// (2vb + hh) ^ (2x & 15) = 2 (vb ^ (x & 7)) + hh).  Key block j adds an
+// immediate.
 template <int T, int W>
 __device__ __forceinline__ void mha_k_offsets(uint32_t (&k)[6]) {
   using Tl = MhaTile<T, W>;
@@ -147,9 +151,9 @@ __device__ __forceinline__ void mha_v_offsets(uint32_t (&v)[8]) {
   using Tl = MhaTile<T, W>;
   const uint32_t lane = opaque(threadIdx.x & 63), q = lane >> 4, rr = lane & 15;
   const uint32_t x = 4 * q + (rr >> 2), hh = (rr & 3) >> 1;
-  const uint32_t rowo = Tl::kKn + Tl::kKr + x * 256 + ((hh ^ (x & 1)) << 4) + 8 * (rr & 1);
+  const uint32_t rowo = Tl::kKn + Tl::kKr + x * 256 + (hh << 4) + 8 * (rr & 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = rowo + (((uint32_t)i ^ (x >> 1)) << 5);
+  for (int i = 0; i < 8; ++i) v[i] = rowo + (((uint32_t)i ^ (x & 7)) << 5);
 }
 
 // One tile: scores, online softmax (kMask: some key of the tile lies past
