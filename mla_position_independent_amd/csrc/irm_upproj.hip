@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include "irm_attn.h"
+#include "irm_internal.h"
 #include "irm_launch.h"
 
 namespace irm {
@@ -143,8 +144,10 @@ irm_status launch_kv_upproj(const void* kv, uint64_t kv_rows, const void* w_uk, 
   a.out = static_cast<unsigned char*>(out);
   a.rows = (uint32_t)kv_rows;
   a.n_heads = n_heads;
-  a.row_tiles = (uint32_t)((kv_rows + kUpRows - 1) / kUpRows);
-  hipLaunchKernelGGL(upproj_kernel, dim3(a.row_tiles * n_heads), dim3(kThreads), 0, s, a);
+  const uint64_t tiles = (kv_rows + kUpRows - 1) / kUpRows, grid = tiles * n_heads;
+  if (grid * kThreads > 0xffffffffull) return fail(IRM_EUNSUPPORTED, "irm_mla_kv_upproj: grid too large");
+  a.row_tiles = (uint32_t)tiles;
+  hipLaunchKernelGGL(upproj_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, s, a);
   return launch_check("up-projection kernel");
 }
 
