@@ -340,7 +340,7 @@ def _tiny_chunks(rng):
     return int(rng.integers(1, 8))
 
 
-@pytest.mark.parametrize("heads", [16, 64])
+@pytest.mark.parametrize("heads", [16, 64, 128])
 def test_decode_short_chunks(heads):
     """Chunks of 1..7 rows: most 8-row slices hold three or more deltas, which
     the per-wave trig table (two deltas) cannot cover."""
@@ -361,7 +361,7 @@ def _scaled_queries(w, f):
     return w
 
 
-@pytest.mark.parametrize("heads", [16, 64])
+@pytest.mark.parametrize("heads", [16, 64, 128])
 def test_decode_rescale_paths(heads):
     """The lse bound scales with |q_rope| (the score error of the bf16 k_r is
     linear in it), so it is taken four times wider here."""
