@@ -298,10 +298,16 @@ def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
     tokens = t.total_rows
     alg_bytes = 2 * ROW_BYTES * tokens
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    # the kernel reads each pool run that several entries place once: its
+    # least traffic is those rows read once plus every assembled row written
+    gs = t.gather_stats()
+    min_bytes = ROW_BYTES * (gs["read_rows"] + tokens)
     traffic = measured_traffic("rotate_gather_kernel" + ("" if make is None else ":" + w.name))
     cold_ms, warm1_ms = time_cold(lambda: irm.rotate_gather(t, pool, out=out))
     prep_ms = time_events(lambda: t.prepare(inv))
     upload_ms = time_events(lambda: t.upload(inv, dev_buf=t._dev))
+    log(f"{label}: pool rows read {gs['read_rows']} of {tokens} assembled ({gs['n_items']} work items); "
+        f"{min_bytes / (kern_ms * 1e-3) / 1e9:.0f} GB/s of least traffic")
     log(f"{label}: {ms:.3f} ms/step, kernel {kern_ms:.3f} ms (median), {achieved:.0f} GB/s; behind a cache scrub "
         f"{cold_ms:.3f} ms, behind a small kernel {warm1_ms:.3f} ms; prepare {prep_ms:.3f} ms, upload with its "
         f"copy {upload_ms:.3f} ms")
@@ -310,14 +316,17 @@ def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
         "mean_entry_len": round(tokens / max(1, t.n_chunks), 1),
         "table_prepare_ms": round(prep_ms, 4),
         "table_upload_ms": round(upload_ms, 4),
-        # the host image copied by the upload: everything before the trig and
-        # row-map regions, which the device passes write (256-byte aligned regions)
-        "table_h2d_bytes": int(t.device_bytes - 256 * t.n_chunks - -(-16 * (t.total_rows + 64) // 256) * 256),
+        # the host image copied by the upload (the trig, row-map and work-item
+        # regions are written by the device passes)
+        "table_h2d_bytes": int(gs["host_bytes"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "rotate_gather_kernel",
                      "kernel_ms_median": round(kern_ms, 4), "kernel_ms_mean": round(kern_mean, 4),
                      "algorithmic_bytes_per_launch": alg_bytes,
+                     "pool_rows_read": int(gs["read_rows"]),
+                     "min_traffic_bytes_per_launch": int(min_bytes),
+                     "min_traffic_frac": round(min_bytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "cold_cache_kernel_ms": round(cold_ms, 4),
                      "cold_cache_frac": round(alg_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "warm_behind_small_kernel_ms": round(warm1_ms, 4)},

@@ -143,6 +143,19 @@ irm_status irm_table_info(const irm_table* t, uint32_t* n_seq, uint32_t* n_chunk
                           uint64_t* total_rows, uint32_t* max_seq_len,
                           size_t* device_bytes);
 
+/*
+ * How irm_rotate_gather works through a table (any pointer may be NULL):
+ *   n_groups = work records (entries that start at the same pool row form a
+ *   group, cut into records of at most 256 rows); n_items = one-wave work
+ *   items of up to 8 rows; read_rows = pool rows one irm_rotate_gather call
+ *   reads (each record's rows once, for all its entries; total_rows minus
+ *   this is the chunk reuse across the batch); host_bytes = bytes
+ *   irm_table_upload copies to the device (the rest of device_bytes is
+ *   written there by the table's own kernels).  Needs no GPU.
+ */
+irm_status irm_table_gather_stats(const irm_table* t, uint32_t* n_groups, uint64_t* n_items, uint64_t* read_rows,
+                                  size_t* host_bytes);
+
 /* host out seq_base[n_seq + 1]: first assembled row of each sequence. */
 irm_status irm_table_seq_base(const irm_table* t, uint64_t* seq_base);
 
@@ -201,7 +214,9 @@ irm_status irm_table_gather_index(const irm_table* t, int64_t* pool_row, int32_t
  *   computed in float and rounded to bf16;
  *   device kr_f32 optional float [total_rows][64]: the rotated k_r before
  *   rounding (NULL in production).
- * Buffers must not overlap.  Requires an uploaded table.
+ * Buffers must not overlap.  Requires an uploaded table.  Entries that
+ * start at the same pool row (a registry chunk several requests place) are
+ * read from the pool once per call and written to every placement.
  */
 irm_status irm_rotate_gather(const irm_table* t, const void* pool, uint64_t pool_rows,
                              void* out_kv, float* kr_f32, void* stream);

@@ -33,7 +33,7 @@ CHUNK_DTYPE = np.dtype(
 
 EXPORTS = (
     "irm_last_error", "irm_rope_inv_freq", "irm_rope_inv_freq_dim", "irm_table_create", "irm_table_destroy",
-    "irm_table_info", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
+    "irm_table_info", "irm_table_gather_stats", "irm_table_seq_base", "irm_table_expand_host", "irm_table_upload",
     "irm_table_set_rope", "irm_table_prepare",
     "irm_table_gather_index", "irm_rotate_gather", "irm_mla_decode_workspace",
     "irm_mla_decode", "irm_mla_decode_noalloc", "irm_mla_prefill_tail", "irm_mla_prefill_assembled", "irm_gqa_workspace",
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         "irm_table_create": (ctypes.c_int, [vp, u32, vp, u32, u64, P(vp)]),
         "irm_table_destroy": (ctypes.c_int, [vp]),
         "irm_table_info": (ctypes.c_int, [vp, P(u32), P(u32), P(u64), P(u32), P(sz)]),
+        "irm_table_gather_stats": (ctypes.c_int, [vp, P(u32), P(u64), P(u64), P(sz)]),
         "irm_table_seq_base": (ctypes.c_int, [vp, vp]),
         "irm_table_expand_host": (ctypes.c_int, [vp, vp, vp, vp]),
         "irm_table_upload": (ctypes.c_int, [vp, vp, vp, sz, vp]),
@@ -189,6 +190,15 @@ class Table:
         self.total_rows, self.max_seq_len, self.device_bytes = total.value, mx.value, dbytes.value
         self.pool_rows = int(pool_rows)
         self._dev = None
+
+    def gather_stats(self) -> dict:
+        """How the rotate-gather works through this table: work records and
+        items, the pool rows one call reads (each shared run once) and the
+        bytes an upload copies from the host."""
+        g, it, rr, hb = ctypes.c_uint32(), ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_size_t()
+        _check(lib().irm_table_gather_stats(self._h, ctypes.byref(g), ctypes.byref(it), ctypes.byref(rr),
+                                            ctypes.byref(hb)), "irm_table_gather_stats")
+        return {"n_groups": g.value, "n_items": it.value, "read_rows": rr.value, "host_bytes": hb.value}
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -40,6 +40,9 @@ struct Image {
   const uint32_t* block_map;
   const float2* trig;
   const uint4* rowmap;  // {pool row, delta, entry or kNoRot, 0} per assembled row
+  const GatherGroup* groups;
+  const uint32_t* members;
+  const uint4* items;   // {first pool row, rows | members << 4, first member, row offset}
   uint32_t n_entries;
 };
 
@@ -53,6 +56,9 @@ inline Image image_of(const irm_table* t) {
   im.block_map = reinterpret_cast<const uint32_t*>(d + t->layout.off_block_map);
   im.trig = reinterpret_cast<const float2*>(d + t->layout.off_trig);
   im.rowmap = reinterpret_cast<const uint4*>(d + t->layout.off_rowmap);
+  im.groups = reinterpret_cast<const GatherGroup*>(d + t->layout.off_groups);
+  im.members = reinterpret_cast<const uint32_t*>(d + t->layout.off_members);
+  im.items = reinterpret_cast<const uint4*>(d + t->layout.off_items);
   im.n_entries = t->n_chunks;
   return im;
 }

@@ -9,9 +9,11 @@
 // below 32 are always fresh (gist.science summary section 2.2; gentlecold.top
 // section 7).
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <numeric>
 #include <string>
 
 #include "irm_internal.h"
@@ -152,6 +154,51 @@ extern "C" irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunk
     }
   }
 
+  // gather groups: entries sorted by first pool row (ties by index), one
+  // group per distinct first row, cut into records of kGroupRows rows
+  // (the rotate-gather loads each record's rows once for all its members)
+  std::vector<uint32_t> members(n_chunks);
+  std::iota(members.begin(), members.end(), 0u);
+  std::sort(members.begin(), members.end(), [&](uint32_t a, uint32_t b) {
+    return t->entries[a].pool_row != t->entries[b].pool_row ? t->entries[a].pool_row < t->entries[b].pool_row
+                                                            : a < b;
+  });
+  std::vector<irm::GatherGroup> groups;
+  for (uint32_t i = 0; i < n_chunks;) {
+    uint32_t j = i, rows = 0;
+    while (j < n_chunks && t->entries[members[j]].pool_row == t->entries[members[i]].pool_row) {
+      rows = std::max(rows, t->entries[members[j]].len);
+      ++j;
+    }
+    for (uint32_t r0 = 0; r0 < rows; r0 += irm::kGroupRows) {
+      irm::GatherGroup g{};
+      g.pool_row = t->entries[members[i]].pool_row + r0;
+      g.n_rows = std::min(irm::kGroupRows, rows - r0);
+      g.member_off = i;
+      g.n_members = j - i;
+      g.row_off = r0;
+      groups.push_back(g);
+    }
+    i = j;
+  }
+  // Records run in the assembled order of their first member, so that most
+  // rows are written in sequence as a plain gather writes them and only the
+  // further placements of a chunk land elsewhere (measured on the 64 x
+  // 32768-token batch: 0.737 ms against 0.755 ms in pool-row order)
+  std::stable_sort(groups.begin(), groups.end(), [&](const irm::GatherGroup& x, const irm::GatherGroup& y) {
+    return (uint64_t)t->entries[members[x.member_off]].out_row + x.row_off <
+           (uint64_t)t->entries[members[y.member_off]].out_row + y.row_off;
+  });
+  uint64_t items = 0, read_rows = 0;
+  for (irm::GatherGroup& g : groups) {
+    g.item_off = (uint32_t)items;
+    items += (g.n_rows + irm::kItemRows - 1) / irm::kItemRows;
+    read_rows += g.n_rows;
+  }
+  t->n_groups = (uint32_t)groups.size();
+  t->n_items = items;
+  t->read_rows = read_rows;
+
   // image layout and host image
   irm::ImageLayout& L = t->layout;
   size_t off = 0;
@@ -159,8 +206,11 @@ extern "C" irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunk
   L.off_seq_first = off; off = irm::align_up(off + sizeof(uint32_t) * ((size_t)n_seq + 1));
   L.off_seq_base = off;  off = irm::align_up(off + sizeof(uint32_t) * ((size_t)n_seq + 1));
   L.off_block_map = off; off = irm::align_up(off + sizeof(uint32_t) * t->block_map.size());
+  L.off_groups = off;    off = irm::align_up(off + sizeof(irm::GatherGroup) * groups.size());
+  L.off_members = off;   off = irm::align_up(off + sizeof(uint32_t) * (size_t)n_chunks);
   L.off_trig = off;      off = irm::align_up(off + sizeof(float) * 2 * irm::kPairs * (size_t)n_chunks);
   L.off_rowmap = off;    off = irm::align_up(off + sizeof(uint32_t) * 4 * ((size_t)total + 64));
+  L.off_items = off;     off = irm::align_up(off + sizeof(uint32_t) * 4 * (size_t)items);
   L.bytes = off;
   t->image.assign(L.off_trig, 0);
   if (n_chunks)
@@ -169,6 +219,9 @@ extern "C" irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunk
   std::memcpy(t->image.data() + L.off_seq_base, t->seq_base.data(), sizeof(uint32_t) * (n_seq + 1));
   std::memcpy(t->image.data() + L.off_block_map, t->block_map.data(),
               sizeof(uint32_t) * t->block_map.size());
+  if (!groups.empty())
+    std::memcpy(t->image.data() + L.off_groups, groups.data(), sizeof(irm::GatherGroup) * groups.size());
+  if (n_chunks) std::memcpy(t->image.data() + L.off_members, members.data(), sizeof(uint32_t) * n_chunks);
   *out = t;
   return IRM_OK;
 }
@@ -187,6 +240,16 @@ extern "C" irm_status irm_table_info(const irm_table* t, uint32_t* n_seq, uint32
   if (total_rows) *total_rows = t->total_rows;
   if (max_seq_len) *max_seq_len = t->max_seq_len;
   if (device_bytes) *device_bytes = t->layout.bytes;
+  return IRM_OK;
+}
+
+extern "C" irm_status irm_table_gather_stats(const irm_table* t, uint32_t* n_groups, uint64_t* n_items,
+                                             uint64_t* read_rows, size_t* host_bytes) {
+  if (!t) return fail(IRM_EINVAL, "irm_table_gather_stats: table is NULL");
+  if (n_groups) *n_groups = t->n_groups;
+  if (n_items) *n_items = t->n_items;
+  if (read_rows) *read_rows = t->read_rows;
+  if (host_bytes) *host_bytes = t->image.size();
   return IRM_OK;
 }
 

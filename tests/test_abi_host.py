@@ -304,3 +304,33 @@ def test_check_out_refuses_outputs_the_kernels_could_overrun():
     with pytest.raises(TypeError):
         irm.check_out(np.zeros((3, 4)), (3, 4), "cpu")
     irm.check_out(torch.empty(10, dtype=torch.uint8), (10,), "cpu", "workspace", torch.uint8)
+
+
+def test_table_gather_stats_counts_shared_runs():
+    """Entries that start at the same pool row are read once by the
+    rotate-gather.  Groups of the table below, counted by hand: pool row 0
+    (two fresh placements of 40 rows) 40 rows, 5 items; pool row 100 (600,
+    300, 257, 600 and 1 rows) 600 rows in records of 256, 256 and 88 rows,
+    32 + 32 + 11 items; pool row 800 (50, 10, 50) 50 rows, 7 items; pool row
+    900 (1, 1) 1 row, 1 item; pool row 1000 (32) 4 items; pool row 150 (100,
+    a run starting inside the 600-row chunk: its own group) 13 items."""
+    rng = np.random.default_rng(41)
+    src = lambda: int(rng.integers(0, 131072))
+    s0 = [(0, 40, 0, 0, FRESH), (100, 600, src(), 40, 0), (800, 50, src(), 640, 0), (100, 300, src(), 690, 0),
+          (900, 1, src(), 990, 0)]
+    s1 = [(1000, 32, 0, 0, FRESH), (100, 257, src(), 32, 0), (900, 1, src(), 289, 0), (800, 10, src(), 290, 0),
+          (150, 100, src(), 300, 0), (800, 50, src(), 400, 0)]
+    s2 = [(0, 40, 0, 0, FRESH), (100, 600, src(), 40, 0), (100, 1, src(), 640, 0)]
+    chunks = np.array(s0 + s1 + s2, dtype=CHUNK_DTYPE)
+    t = irm.Table(chunks, np.array([0, len(s0), len(s0) + len(s1), len(chunks)], np.uint32), 1100)
+    st = t.gather_stats()
+    assert st["n_groups"] == 8
+    assert st["n_items"] == 5 + 75 + 7 + 1 + 4 + 13
+    assert st["read_rows"] == 40 + 600 + 50 + 1 + 32 + 100
+    assert t.total_rows == 991 + 450 + 641
+    assert 32 * len(chunks) < st["host_bytes"] < t.device_bytes
+    # no shared starts: every assembled row is read once
+    u = irm.Table(np.array([(0, 40, 0, 0, FRESH), (40, 300, 9, 40, 0)], dtype=CHUNK_DTYPE),
+                  np.array([0, 2], np.uint32), 400)
+    su = u.gather_stats()
+    assert su["read_rows"] == u.total_rows == 340 and su["n_groups"] == 1 + 2 and su["n_items"] == 5 + 32 + 6

@@ -136,6 +136,37 @@ def test_rotate_gather_edge_cases():
     assert o.shape[0] == 0
 
 
+def test_rotate_gather_shared_chunks():
+    """Entries that place the same pool rows (one registry chunk reused by
+    several requests, or twice in one) are loaded once and written to every
+    placement: a 600-row chunk (cut into several work records) placed whole,
+    truncated to 300 and to 257 rows and once from its middle (another
+    group), a 50-row chunk whole and truncated to 10, a one-row chunk twice,
+    and a fresh run placed in two sequences; every row against the oracle."""
+    rng = np.random.default_rng(41)
+    src = lambda: int(rng.integers(0, 131072))
+    s0 = [(0, 40, 0, 0, FRESH), (100, 600, src(), 40, 0), (800, 50, src(), 640, 0), (100, 300, src(), 690, 0),
+          (900, 1, src(), 990, 0)]
+    s1 = [(1000, 32, 0, 0, FRESH), (100, 257, src(), 32, 0), (900, 1, src(), 289, 0), (800, 10, src(), 290, 0),
+          (150, 100, src(), 300, 0), (800, 50, src(), 400, 0)]
+    s2 = [(0, 40, 0, 0, FRESH), (100, 600, src(), 40, 0), (100, 1, src(), 640, 0)]
+    chunks = np.array(s0 + s1 + s2, dtype=CHUNK_DTYPE)
+    seq_first = np.array([0, len(s0), len(s0) + len(s1), len(chunks)], np.uint32)
+    from synth import randn_bf16, Workload
+    w = Workload("shared", randn_bf16(rng, (1100, 576)), chunks, seq_first)
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    out, kr = irm.rotate_gather(t, pool, kr_f32=True)
+    out2 = irm.rotate_gather(t, pool)
+    pr, de = t.gather_index()
+    _sync()
+    ob = irm.from_device_bf16(out)
+    gather, delta = _check_gather(w, ob, kr.cpu().numpy())
+    assert np.array_equal(ob, irm.from_device_bf16(out2))
+    assert np.array_equal(pr.cpu().numpy(), gather)
+    assert np.array_equal(de.cpu().numpy().astype(np.int64), delta)
+
+
 def test_rotate_gather_custom_inv_freq():
     """A model's own rotary table (here fp32-rounded frequencies) is honoured."""
     w = random_table(77, [700, 300])
