@@ -41,7 +41,8 @@ CSRC = os.path.join(ROOT, "mla_position_independent_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources that define each timed kernel (a counter record is valid only for these bytes)
 KERNEL_SOURCES = {
-    "rotate_gather_kernel": ["irm_gather.hip", "irm_device.h"],
+    # the gather's reads follow the host's grouping of the entries (irm_table.cpp)
+    "rotate_gather_kernel": ["irm_gather.hip", "irm_device.h", "irm_table.cpp", "irm_internal.h"],
     "decode_private_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
     "decode_shared_kernel": ["irm_decode.hip", "irm_attn.h", "irm_device.h"],
     "prefill_kernel": ["irm_prefill.hip", "irm_attn.h", "irm_device.h"],

@@ -146,10 +146,10 @@ irm_status irm_table_info(const irm_table* t, uint32_t* n_seq, uint32_t* n_chunk
 /*
  * How irm_rotate_gather works through a table (any pointer may be NULL):
  *   n_groups = work records (entries that start at the same pool row form a
- *   group, cut into records of at most 256 rows); n_items = one-wave work
- *   items of up to 8 rows; read_rows = pool rows one irm_rotate_gather call
- *   reads (each record's rows once, for all its entries; total_rows minus
- *   this is the chunk reuse across the batch); host_bytes = bytes
+ *   group, cut into records of at most 256 rows and 8 entries); n_items =
+ *   one-wave work items of up to 8 rows; read_rows = pool rows one
+ *   irm_rotate_gather call reads (each record's rows once, for all its
+ *   entries; total_rows minus this is the chunk reuse the call exploits); host_bytes = bytes
  *   irm_table_upload copies to the device (the rest of device_bytes is
  *   written there by the table's own kernels).  Needs no GPU.
  */
@@ -216,7 +216,8 @@ irm_status irm_table_gather_index(const irm_table* t, int64_t* pool_row, int32_t
  *   rounding (NULL in production).
  * Buffers must not overlap.  Requires an uploaded table.  Entries that
  * start at the same pool row (a registry chunk several requests place) are
- * read from the pool once per call and written to every placement.
+ * read from the pool once per call (once per 8 placements) and written to
+ * every placement.
  */
 irm_status irm_rotate_gather(const irm_table* t, const void* pool, uint64_t pool_rows,
                              void* out_kv, float* kr_f32, void* stream);

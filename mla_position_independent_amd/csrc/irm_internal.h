@@ -26,9 +26,9 @@ static_assert(sizeof(DevEntry) == 32, "device entry is 32 bytes");
 // The rotate-gather reads each pool row once per table however many entries
 // place it: entries are grouped by their first pool row (a registry chunk
 // reused by several requests), and a group is cut into records of at most
-// kGroupRows rows.  Every record lists the group's members (entry indices)
-// and is worked on in items of kItemRows rows, each loaded once and written
-// to every member.  Members may be shorter than the group (a truncated
+// kGroupRows rows and kGroupMembers members.  Every record lists its members
+// (entry indices) and is worked on in items of kItemRows rows, each loaded
+// once and written to every member.  Members may be shorter than the group (a truncated
 // chunk): a member takes the rows below its own length.
 struct GatherGroup {
   uint32_t pool_row;    // first pool row of the record
@@ -41,6 +41,7 @@ struct GatherGroup {
 };
 static_assert(sizeof(GatherGroup) == 32, "gather group record is 32 bytes");
 constexpr uint32_t kGroupRows = 256;
+constexpr uint32_t kGroupMembers = 8;
 constexpr uint32_t kItemRows = 8;
 
 // Rows per block of the block map: block_map[b] is the entry that holds

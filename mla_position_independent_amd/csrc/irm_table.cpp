@@ -165,19 +165,24 @@ extern "C" irm_status irm_table_create(const irm_chunk* chunks, uint32_t n_chunk
   });
   std::vector<irm::GatherGroup> groups;
   for (uint32_t i = 0; i < n_chunks;) {
-    uint32_t j = i, rows = 0;
-    while (j < n_chunks && t->entries[members[j]].pool_row == t->entries[members[i]].pool_row) {
-      rows = std::max(rows, t->entries[members[j]].len);
-      ++j;
-    }
-    for (uint32_t r0 = 0; r0 < rows; r0 += irm::kGroupRows) {
-      irm::GatherGroup g{};
-      g.pool_row = t->entries[members[i]].pool_row + r0;
-      g.n_rows = std::min(irm::kGroupRows, rows - r0);
-      g.member_off = i;
-      g.n_members = j - i;
-      g.row_off = r0;
-      groups.push_back(g);
+    uint32_t j = i;
+    while (j < n_chunks && t->entries[members[j]].pool_row == t->entries[members[i]].pool_row) ++j;
+    // at most kGroupMembers placements per record: a run that many entries
+    // place is read once per kGroupMembers of them, which bounds the writes
+    // of one work item
+    for (uint32_t m0 = i; m0 < j; m0 += irm::kGroupMembers) {
+      const uint32_t m1 = std::min(j, m0 + irm::kGroupMembers);
+      uint32_t rows = 0;
+      for (uint32_t m = m0; m < m1; ++m) rows = std::max(rows, t->entries[members[m]].len);
+      for (uint32_t r0 = 0; r0 < rows; r0 += irm::kGroupRows) {
+        irm::GatherGroup g{};
+        g.pool_row = t->entries[members[i]].pool_row + r0;
+        g.n_rows = std::min(irm::kGroupRows, rows - r0);
+        g.member_off = m0;
+        g.n_members = m1 - m0;
+        g.row_off = r0;
+        groups.push_back(g);
+      }
     }
     i = j;
   }

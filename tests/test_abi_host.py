@@ -334,3 +334,22 @@ def test_table_gather_stats_counts_shared_runs():
                   np.array([0, 2], np.uint32), 400)
     su = u.gather_stats()
     assert su["read_rows"] == u.total_rows == 340 and su["n_groups"] == 1 + 2 and su["n_items"] == 5 + 32 + 6
+
+
+def test_table_gather_stats_caps_placements_per_record():
+    """A run placed by 20 entries (a prompt every request shares) is read once
+    per 8 placements: records of 8, 8 and 4 members; the 4-row tail of the
+    40-row run placed by the longest members only is read by their record."""
+    seq_first = [0]
+    chunks = []
+    for s in range(20):
+        n = 40 if s < 3 else 36          # the first record's first three members are longer
+        chunks += [(1000 + 40 * s, 32, 0, 0, FRESH), (0, n, 5, 32, 0)]
+        seq_first.append(len(chunks))
+    t = irm.Table(np.array(chunks, dtype=CHUNK_DTYPE), np.array(seq_first, np.uint32), 2000)
+    st = t.gather_stats()
+    # 20 fresh runs of 32 rows (own groups, 4 items each) + the shared run: members 0-7 (40 rows,
+    # 5 items), 8-15 (36 rows, 5 items), 16-19 (36 rows, 5 items)
+    assert st["n_groups"] == 20 + 3
+    assert st["n_items"] == 20 * 4 + 5 + 5 + 5
+    assert st["read_rows"] == 20 * 32 + 40 + 36 + 36

@@ -167,6 +167,26 @@ def test_rotate_gather_shared_chunks():
     assert np.array_equal(de.cpu().numpy().astype(np.int64), delta)
 
 
+def test_rotate_gather_popular_chunk():
+    """A 40-row run placed by 20 requests at 20 different deltas (a prompt
+    every request shares), read once per 8 placements, and their fresh
+    heads: every row against the oracle."""
+    rng = np.random.default_rng(43)
+    seq_first, chunks = [0], []
+    for s in range(20):
+        n = 40 if s < 3 else 36
+        chunks += [(1000 + 40 * s, 32, 0, 0, FRESH), (0, n, int(rng.integers(0, 131072)), 32, 0)]
+        seq_first.append(len(chunks))
+    from synth import randn_bf16, Workload
+    w = Workload("popular", randn_bf16(rng, (2000, 576)), np.array(chunks, dtype=CHUNK_DTYPE),
+                 np.array(seq_first, np.uint32))
+    pool = irm.to_device_bf16(w.pool)
+    t = _table(w)
+    out, kr = irm.rotate_gather(t, pool, kr_f32=True)
+    _sync()
+    _check_gather(w, irm.from_device_bf16(out), kr.cpu().numpy())
+
+
 def test_rotate_gather_custom_inv_freq():
     """A model's own rotary table (here fp32-rounded frequencies) is honoured."""
     w = random_table(77, [700, 300])
