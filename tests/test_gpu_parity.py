@@ -830,6 +830,43 @@ def test_decode_graph_replay():
         assert np.array_equal(got, irm.from_device_bf16(eager)), rep
 
 
+def test_rotate_gather_graph_replay():
+    """The table prepare (row map, trig rows, gather work items) and the
+    grouped rotate-gather captured in one HIP graph and replayed: with the
+    device passes cleared between replays, new pool values and eager gathers
+    in between, every replay matches the eager result bit for bit."""
+    import torch
+    w = random_table(17, [1500, 900, 2600], p_hit=0.8)
+    pool = irm.to_device_bf16(w.pool)
+    inv = irm.rope_inv_freq(w.theta)
+    t = _table(w)
+    out_g = torch.empty((t.total_rows, 576), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        t.prepare(inv)
+        irm.rotate_gather(t, pool, out=out_g)
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        t.prepare(inv)
+        irm.rotate_gather(t, pool, out=out_g)
+    rng = np.random.default_rng(18)
+    host_bytes = t.gather_stats()["host_bytes"]   # the image past the host copy is written by the device passes
+    for rep in range(4):
+        t._dev[host_bytes:].zero_()
+        if rep >= 2:
+            from synth import randn_bf16
+            pool.copy_(irm.to_device_bf16(randn_bf16(rng, tuple(pool.shape))))
+        graph.replay()
+        _sync()
+        got = irm.from_device_bf16(out_g).copy()
+        eager = irm.rotate_gather(t, pool)
+        _sync()
+        assert np.array_equal(got, irm.from_device_bf16(eager)), rep
+
+
 def test_decode_workspace_reuse_across_split_counts():
     """One workspace serves consecutive decodes with different split counts;
     no call may depend on what an earlier call left in it."""
