@@ -137,7 +137,11 @@ class ClockSampler:
     runs (the part lowers its clock under sustained load, so MFMA-bound
     rates depend on it).  Reads the current level of pp_dpm_sclk or the
     hwmon sclk input of the first amdgpu card that has one; reports nothing
-    where neither exists."""
+    where neither exists.  The card's power reading (hwmon power1_average or
+    power1_input) and its power cap are sampled beside it where they exist;
+    that reading is the firmware's running average, which trails a leg of a
+    few tens of milliseconds, so it is context for the clock, not a measure
+    of the leg's own draw."""
 
     def __init__(self, period_s: float = 0.002):
         import glob
@@ -158,6 +162,19 @@ class ClockSampler:
                 self.source = ("dpm", os.path.join(dev, "pp_dpm_sclk"))
             if self.source is not None:
                 break
+        self.power_path = self.cap_w = None
+        self.power = []
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            for h in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+                for name in ("power1_average", "power1_input"):
+                    if self.power_path is None and os.path.exists(os.path.join(h, name)):
+                        self.power_path = os.path.join(h, name)
+                        try:
+                            self.cap_w = int(open(os.path.join(h, "power1_cap")).read().strip()) / 1e6
+                        except (OSError, ValueError):
+                            pass
+            if self.power_path is not None:
+                break
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -176,29 +193,48 @@ class ClockSampler:
     def _run(self):
         while not self._stop.is_set():
             try:
-                v = self._read()
+                v = self._read() if self.source is not None else None
                 if v:
                     self.samples.append(v)
+                if self.power_path is not None:
+                    with open(self.power_path) as f:
+                        self.power.append(int(f.read().strip()) / 1e6)
             except (OSError, ValueError, IndexError):
                 pass
             self._stop.wait(self.period)
 
     def __enter__(self):
-        if self.source is not None:
+        if self.source is not None or self.power_path is not None:
             self._thread.start()
         return self
 
     def __exit__(self, *exc):
-        if self.source is not None:
+        if self.source is not None or self.power_path is not None:
             self._stop.set()
             self._thread.join()
 
     def summary(self):
-        if not self.samples:
+        if not self.samples and not self.power:
             return None
-        v = sorted(self.samples)
-        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
-                "source": self.source[0]}
+        res = {}
+        if self.samples:
+            v = sorted(self.samples)
+            res.update({"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "samples": len(v),
+                        "source": self.source[0]})
+        if self.power:
+            pw = sorted(self.power)
+            res.update({"power_median_w": round(pw[len(pw) // 2], 1), "power_max_w": round(pw[-1], 1),
+                        "power_cap_w": self.cap_w})
+        return res
+
+
+def frac_at_clock(frac: float, clk):
+    """A fraction of the 2.4 GHz peak restated against the peak at the shader
+    clock sampled during the timed loop (the part runs sustained MFMA-heavy
+    kernels below 2.4 GHz); None without a clock sample."""
+    if not clk or not clk.get("median_mhz"):
+        return None
+    return round(frac * 2400.0 / clk["median_mhz"], 4)
 
 
 def time_leg(fn, steps: int, warmup: int, inner_events: bool = True):
@@ -436,6 +472,7 @@ def leg_decode(args, irm, torch, synth, name, make):
                      "warm_behind_small_kernel_ms": round(warm1_ms, 4)},
         "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
         "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "mfma_frac_at_sampled_clock": frac_at_clock(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, clk),
         "rotation_on_load": rot,
         "sclk": clk,
     }
@@ -538,7 +575,8 @@ def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = T
                      "traffic": measured_traffic("prefill_kernel"), "kernel": "prefill_kernel (assembled cache)",
                      "kernel_ms_median": round(kern_ms, 4), "kernel_ms_mean": round(kern_mean, 4),
                      "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": ROW_BYTES * t.total_rows + nq * H * (576 + 512) * 2},
+                     "algorithmic_bytes_per_launch": ROW_BYTES * t.total_rows + nq * H * (576 + 512) * 2,
+                     "frac_at_sampled_clock": frac_at_clock(achieved / MFMA_BF16_PEAK_TFS, clk)},
         "sclk": clk,
     }
 
@@ -592,7 +630,8 @@ def leg_nonabsorbed(args, irm, torch, synth):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
                      "traffic": measured_traffic("mha_prefill_kernel"), "kernel": "mha_prefill_kernel",
-                     "algorithmic_flops_per_launch": flops},
+                     "algorithmic_flops_per_launch": flops,
+                     "frac_at_sampled_clock": frac_at_clock(achieved / MFMA_BF16_PEAK_TFS, clk)},
         "sclk": clk,
     }
 
