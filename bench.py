@@ -237,15 +237,38 @@ def frac_at_clock(frac: float, clk):
     return round(frac * 2400.0 / clk["median_mhz"], 4)
 
 
-def time_leg(fn, steps: int, warmup: int, inner_events: bool = True):
-    """Run fn(ev_mid_or_None) warmup+steps times.  Returns wall ms per step
-    (synchronised on both sides of the timed region), the median event time
-    of the part fn brackets (ms), the mean of those event times, and the
-    shader clock sampled during the timed region."""
+# After the GPU has idled (while a leg draws its inputs on the host) its
+# shader clock ramps up over the first tens of milliseconds of sustained
+# work: the long decode's first 20 calls after 3 warm-up calls take 0.45 ms
+# each against 0.40 ms after 200.  The decode and prefill legs therefore warm
+# up for at least this long, so that their timed loops see the rate that a
+# running decode or prefill loop sees; the headline step keeps exactly the
+# warm-up steps it is given.
+LEG_WARM_MS = 150.0
+
+
+def time_leg(fn, steps: int, warmup: int, inner_events: bool = True, min_warm_ms: float = 0.0):
+    """Run fn(ev_mid_or_None) warmup times, then more untimed calls until at
+    least min_warm_ms have passed since the first, then steps timed calls.
+    Returns wall ms per timed step (synchronised on both sides of the timed
+    region), the median event time of the part fn brackets (ms), the mean of
+    those event times, the shader clock sampled during the timed region, and
+    the number of untimed calls made."""
     import torch
+    t_w = time.perf_counter()
+    n_warm = 0
     for _ in range(warmup):
         fn(None)
+        n_warm += 1
     torch.cuda.synchronize()
+    while (time.perf_counter() - t_w) * 1e3 < min_warm_ms:
+        # enqueue about the calls the remaining time holds, at the rate so far
+        per_ms = (time.perf_counter() - t_w) * 1e3 / max(n_warm, 1)
+        more = max(1, min(1000, int((min_warm_ms - (time.perf_counter() - t_w) * 1e3) / max(per_ms, 1e-3)) + 1))
+        for _ in range(more):
+            fn(None)
+            n_warm += 1
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     with ClockSampler() as clk:
         t0 = time.perf_counter()
@@ -256,7 +279,7 @@ def time_leg(fn, steps: int, warmup: int, inner_events: bool = True):
     kern = sorted(a.elapsed_time(b) for a, b in evs) if inner_events else []
     med = kern[len(kern) // 2] if kern else None
     mean = sum(kern) / len(kern) if kern else None
-    return (t1 - t0) * 1e3 / steps, med, mean, clk.summary()
+    return (t1 - t0) * 1e3 / steps, med, mean, clk.summary(), n_warm
 
 
 _SCRUB = []
@@ -331,7 +354,7 @@ def leg_gather(args, irm, torch, synth, make=None, label="rotate-gather"):
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms, kern_mean, clk = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, kern_mean, clk, _ = time_leg(step, args.steps, args.warmup)
     tokens = t.total_rows
     alg_bytes = 2 * ROW_BYTES * tokens
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
@@ -422,7 +445,7 @@ def leg_decode(args, irm, torch, synth, name, make):
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms, kern_mean, clk = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, kern_mean, clk, n_warm = time_leg(step, args.steps, args.warmup, min_warm_ms=LEG_WARM_MS)
     cold_ms, warm1_ms = time_cold(lambda: step(None))
 
     # the price of the rotation on load
@@ -475,6 +498,7 @@ def leg_decode(args, irm, torch, synth, name, make):
         "mfma_frac_at_sampled_clock": frac_at_clock(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, clk),
         "rotation_on_load": rot,
         "sclk": clk,
+        "warmup_calls": n_warm,
     }
 
 
@@ -498,7 +522,7 @@ def leg_tiny(args, irm, torch, synth):
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms, _, _ = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, _, _, _ = time_leg(step, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -549,11 +573,11 @@ def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = T
 
     n_steps, n_warm = max(3, args.steps // 4), min(args.warmup, 2)
     if not assembled:   # profiling the fused kernel alone
-        fused_ms = time_leg(fused_call, n_steps, n_warm)[1]
+        fused_ms = time_leg(fused_call, n_steps, n_warm, min_warm_ms=LEG_WARM_MS)[1]
         log(f"tail-prefill, rotation on load in one kernel: {fused_ms:.3f} ms")
         return None
-    ms, kern_ms, kern_mean, clk = time_leg(step, n_steps, n_warm)
-    fused_ms = time_leg(fused_call, n_steps, 1)[1] if fused else None
+    ms, kern_ms, kern_mean, clk, warm_calls = time_leg(step, n_steps, n_warm, min_warm_ms=LEG_WARM_MS)
+    fused_ms = time_leg(fused_call, n_steps, 1, min_warm_ms=LEG_WARM_MS)[1] if fused else None
     pairs = nq * w.q_pos0 + nq * (nq + 1) // 2      # visible (query, key) pairs
     flops = pairs * H * 2 * (576 + 512)
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -578,6 +602,7 @@ def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = T
                      "algorithmic_bytes_per_launch": ROW_BYTES * t.total_rows + nq * H * (576 + 512) * 2,
                      "frac_at_sampled_clock": frac_at_clock(achieved / MFMA_BF16_PEAK_TFS, clk)},
         "sclk": clk,
+        "warmup_calls": warm_calls,
     }
 
 
@@ -614,8 +639,8 @@ def leg_nonabsorbed(args, irm, torch, synth):
             ev[1].record()
 
     n_steps = max(3, args.steps // 2)
-    up_ms = time_leg(up, n_steps, min(args.warmup, 2))[1]
-    _, kern_ms, _, clk = time_leg(attend, n_steps, min(args.warmup, 2))
+    up_ms = time_leg(up, n_steps, min(args.warmup, 2), min_warm_ms=LEG_WARM_MS)[1]
+    _, kern_ms, _, clk, warm_calls = time_leg(attend, n_steps, min(args.warmup, 2), min_warm_ms=LEG_WARM_MS)
     pairs = nq * w.q_pos0 + nq * (nq + 1) // 2
     flops = pairs * H * 2 * (192 + 128)
     up_flops = 2 * kv.shape[0] * 512 * 256 * H
@@ -633,6 +658,7 @@ def leg_nonabsorbed(args, irm, torch, synth):
                      "algorithmic_flops_per_launch": flops,
                      "frac_at_sampled_clock": frac_at_clock(achieved / MFMA_BF16_PEAK_TFS, clk)},
         "sclk": clk,
+        "warmup_calls": warm_calls,
     }
 
 
@@ -658,7 +684,7 @@ def leg_gqa(args, irm, torch, gather):
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms, _, _ = time_leg(step, args.steps, args.warmup)
+    ms, kern_ms, _, _, _ = time_leg(step, args.steps, args.warmup)
     tokens = t.total_rows
     alg_bytes = 2 * 2 * width * tokens
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
