@@ -445,7 +445,7 @@ def leg_decode(args, irm, torch, synth, name, make):
         if ev is not None:
             ev[1].record()
 
-    ms, kern_ms, kern_mean, clk, n_warm = time_leg(step, args.steps, args.warmup, min_warm_ms=LEG_WARM_MS)
+    ms, kern_ms, kern_mean, clk, n_warm = time_leg(step, args.steps, args.warmup, min_warm_ms=args.leg_warm_ms)
     cold_ms, warm1_ms = time_cold(lambda: step(None))
 
     # the price of the rotation on load
@@ -573,11 +573,11 @@ def leg_prefill(args, irm, torch, synth, assembled: bool = True, fused: bool = T
 
     n_steps, n_warm = max(3, args.steps // 4), min(args.warmup, 2)
     if not assembled:   # profiling the fused kernel alone
-        fused_ms = time_leg(fused_call, n_steps, n_warm, min_warm_ms=LEG_WARM_MS)[1]
+        fused_ms = time_leg(fused_call, n_steps, n_warm, min_warm_ms=args.leg_warm_ms)[1]
         log(f"tail-prefill, rotation on load in one kernel: {fused_ms:.3f} ms")
         return None
-    ms, kern_ms, kern_mean, clk, warm_calls = time_leg(step, n_steps, n_warm, min_warm_ms=LEG_WARM_MS)
-    fused_ms = time_leg(fused_call, n_steps, 1, min_warm_ms=LEG_WARM_MS)[1] if fused else None
+    ms, kern_ms, kern_mean, clk, warm_calls = time_leg(step, n_steps, n_warm, min_warm_ms=args.leg_warm_ms)
+    fused_ms = time_leg(fused_call, n_steps, 1, min_warm_ms=args.leg_warm_ms)[1] if fused else None
     pairs = nq * w.q_pos0 + nq * (nq + 1) // 2      # visible (query, key) pairs
     flops = pairs * H * 2 * (576 + 512)
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -639,8 +639,8 @@ def leg_nonabsorbed(args, irm, torch, synth):
             ev[1].record()
 
     n_steps = max(3, args.steps // 2)
-    up_ms = time_leg(up, n_steps, min(args.warmup, 2), min_warm_ms=LEG_WARM_MS)[1]
-    _, kern_ms, _, clk, warm_calls = time_leg(attend, n_steps, min(args.warmup, 2), min_warm_ms=LEG_WARM_MS)
+    up_ms = time_leg(up, n_steps, min(args.warmup, 2), min_warm_ms=args.leg_warm_ms)[1]
+    _, kern_ms, _, clk, warm_calls = time_leg(attend, n_steps, min(args.warmup, 2), min_warm_ms=args.leg_warm_ms)
     pairs = nq * w.q_pos0 + nq * (nq + 1) // 2
     flops = pairs * H * 2 * (192 + 128)
     up_flops = 2 * kv.shape[0] * 512 * 256 * H
@@ -878,6 +878,8 @@ def main():
     ap.add_argument("--cpu-seconds-legs", type=float, default=5.0,
                     help="oracle seconds per decode / prefill leg (its own cpu_baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--leg-warm-ms", type=float, default=LEG_WARM_MS,
+                    help="least warm-up time of the decode and prefill legs (0 in profiling mode)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (for scaling HBM counters) and exit")
     ap.add_argument("--profile", action="store_true",
@@ -918,6 +920,7 @@ def main():
     if args.profile or "gather" not in legs:
         # profiling mode: run the requested legs only, no JSON line, no oracle
         args.no_cpu_baseline = True
+        args.leg_warm_ms = 0.0  # counters and traces need no settled clock
         g = None
         for name in legs:
             if name == "gather":

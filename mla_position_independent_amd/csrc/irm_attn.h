@@ -740,6 +740,10 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
 
   SliceCopies cp;  // copy sources of tile t+2
   int32_t d1;      // delta of this lane's row of tile t+1
+  // (cos, sin) of the four pairs this lane turns, for delta td: deltas change
+  // only at entry boundaries, so most tiles reuse them without an LDS read
+  f32x4_t ta = f32x4_t{1.f, 0.f, 1.f, 0.f}, tb = ta;
+  int32_t td = 0;
 
   // Iteration t: wait for tile t+1 and read the P / C^T fragments and the
   // k_r of tile t+1 in one go.  The first half of the PV MFMAs of tile t-1
@@ -763,7 +767,20 @@ __device__ __forceinline__ void value_stream(const StreamArgs& ra, SplitSmem& sm
     wait_dma_but<B ? kRowMaps : 0>();
     if (rot && !table) slice_rotate<kTileSlice>(ws, sr, row0, sm.s.omega, d1, cd);
     SliceRot rt;
-    if (table) rt = slice_rot_load(ws, sr, row0, d1, cd);
+    if (table) {
+      if (__any(d1 != td)) {
+        const SliceRot x = slice_rot_load(ws, sr, row0, d1, cd);
+        ta = x.a;
+        tb = x.b;
+        td = d1;
+        rt.k = x.k;
+      } else {
+        const uint32_t l = threadIdx.x & 63;
+        rt.k = *reinterpret_cast<const u32x4_t*>(sr + kr_pos(row0 + (l >> 3), l & 7));
+      }
+      rt.a = ta;
+      rt.b = tb;
+    }
     copy_kr(ra, cp, nx + kTileKr, row0);
     auto mid = [&]() {
       // the table's reads are done once the rotated values are stored
