@@ -403,6 +403,25 @@ def test_decode_short_chunks(heads):
         assert np.max(np.abs(l - l_ref)) <= LSE_TOL, S
 
 
+def _short_mixed_chunks(rng):
+    return int(rng.integers(2, 13))
+
+
+@pytest.mark.parametrize("heads", [16, 64, 128])
+def test_decode_repeating_deltas(heads):
+    """Deltas drawn from -3..3 and chunks of 2..12 rows: a rotating lane's
+    delta changes from tile to tile, comes back to an earlier value, and
+    some slices hold three deltas, so the (cos, sin) values the shared-tile
+    kernels keep in registers across tiles are reused, reloaded and
+    bypassed in turn."""
+    w = random_table(35, [900, 333, 64], heads=heads, p_hit=0.9, delta_abs=3, len_fn=_short_mixed_chunks)
+    o_ref, l_ref = _oracle_decode(w, range(w.n_seq))
+    for S in (1, 4):
+        o, l = _gpu_decode(w, S)
+        assert rel_l2(o, o_ref) <= ATTN_TOL, S
+        assert np.max(np.abs(l - l_ref)) <= LSE_TOL, S
+
+
 def _scaled_queries(w, f):
     """Queries times a power of two (exact in bf16): larger score spread, so
     the running maximum moves past the lazy-rescale slack mid-stream."""
